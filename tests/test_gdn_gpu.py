@@ -1,0 +1,195 @@
+"""GPU parity of tr_gdn_replay against the fp64 oracle, through the C ABI.
+
+Tolerances (relative Frobenius error of every (sequence, value head) slice, computed in
+fp64): bf16 inputs with fp32 state -- states <= 2e-3, outputs <= 3e-3; fp32 inputs --
+<= 1e-5 for both.  Outputs are compared as stored (bf16 for bf16 inputs), so the output
+bound includes the bf16 rounding of o itself (about 1.7e-3 relative).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from linear_attention_state_amd import gdn_replay, tail_seqlens
+
+pytestmark = pytest.mark.gpu
+
+STATE_TOL, OUT_TOL, F32_TOL = 2e-3, 3e-3, 1e-5
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    d = np.linalg.norm(a - b)
+    return d / nb if nb > 0 else d
+
+
+def worst_errors(S_gpu, o_gpu, S_ref, o_ref, cu, heads=None):
+    """Worst per-(sequence, head) relative errors of states and outputs."""
+    B = len(cu) - 1
+    Hv = S_ref.shape[1]
+    heads = range(Hv) if heads is None else heads
+    es, eo = 0.0, 0.0
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            es = max(es, rel(S_gpu[b, hi], S_ref[b, hi]))
+            if o_ref is not None and cu[b + 1] > cu[b]:
+                eo = max(eo, rel(o_gpu[cu[b]:cu[b + 1], hi], o_ref[cu[b]:cu[b + 1], hi]))
+    return es, eo
+
+
+def np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_and_compare(inp, state_in=None, q_scale=1.0, stol=STATE_TOL, otol=OUT_TOL, label=""):
+    dev = "cuda"
+    d = inp.to(dev)
+    s_in_dev = None if state_in is None else torch.from_numpy(state_in).float().to(dev)
+    S, o = gdn_replay(d.q, d.k, d.v, d.g, d.beta, inp.cu_seqlens, q_scale=q_scale, state_in=s_in_dev)
+    torch.cuda.synchronize()
+    s_in_ref = None if state_in is None else np.asarray(torch.from_numpy(state_in).float().double())
+    S_ref, o_ref = oracle.gdn(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.g), np64(inp.beta),
+                              inp.cu_seqlens.numpy(), q_scale=q_scale, state_in=s_in_ref)
+    es, eo = worst_errors(np64(S), np64(o), S_ref, o_ref, inp.cu_seqlens.numpy())
+    print("%s worst state err %.3e, worst output err %.3e" % (label, es, eo), flush=True)
+    assert es <= stol, "state error %.3e > %.1e" % (es, stol)
+    assert eo <= otol, "output error %.3e > %.1e" % (eo, otol)
+    return S, o
+
+
+def test_tiny_fp32_case():
+    # 1 LA layer, 1 head, dk = dv = 64, fp32, 256 tokens from zero state
+    inp = synthetic.gdn_inputs([256], 1, 1, 64, 64, dtype=torch.float32, seed=11)
+    run_and_compare(inp, stol=F32_TOL, otol=F32_TOL, label="tiny fp32")
+
+
+RAGGED = [1, 63, 64, 65, 130, 0, 200, 7]
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_bf16_ragged_zero_state(dk, dv):
+    inp = synthetic.gdn_inputs(RAGGED, 2, 4, dk, dv, seed=100 + dk + dv)
+    run_and_compare(inp, label="bf16 ragged %dx%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_bf16_ragged_given_state_and_scale(dk, dv):
+    inp = synthetic.gdn_inputs(RAGGED, 1, 3, dk, dv, seed=7 + dk, q_prescaled=False)
+    rng = np.random.default_rng(5)
+    s_in = (rng.standard_normal((len(RAGGED), 3, dv, dk)) * 0.3).astype(np.float32)
+    run_and_compare(inp, state_in=s_in, q_scale=dk ** -0.5, label="bf16 state_in %dx%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_fp32_ragged(dk, dv):
+    inp = synthetic.gdn_inputs(RAGGED, 2, 4, dk, dv, dtype=torch.float32, seed=3 + dk)
+    rng = np.random.default_rng(9)
+    s_in = (rng.standard_normal((len(RAGGED), 4, dv, dk)) * 0.3).astype(np.float32)
+    run_and_compare(inp, state_in=s_in, q_scale=0.5, stol=F32_TOL, otol=F32_TOL, label="fp32 ragged")
+
+
+def test_single_hit_full_size():
+    # m = 32768, r = 0.05 -> 1,639 tokens, 16 heads, dk = dv = 128, zero state
+    cu, _ = tail_seqlens([32768], 5, 100)
+    inp = synthetic.gdn_inputs([int(cu[1])], 16, 16, 128, 128, seed=2)
+    run_and_compare(inp, label="single hit")
+
+
+def _sampled_parity(inp_dev, cu, seqs, heads, Hqk, Hv, S, o):
+    group = Hv // Hqk
+    worst_s = worst_o = 0.0
+    for b in seqs:
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        for h in heads:
+            j = h // group
+            S_ref, o_ref = oracle.gdn(np64(inp_dev.q[sl, j:j + 1]), np64(inp_dev.k[sl, j:j + 1]),
+                                      np64(inp_dev.v[sl, h:h + 1]), np64(inp_dev.g[sl, h:h + 1]),
+                                      np64(inp_dev.beta[sl, h:h + 1]), [0, sl.stop - sl.start])
+            worst_s = max(worst_s, rel(np64(S[b, h]), S_ref[0, 0]))
+            worst_o = max(worst_o, rel(np64(o[sl, h]), o_ref[:, 0]))
+    return worst_s, worst_o
+
+
+def test_batched_full_size_sampled():
+    # 36 instances x 32 v-heads (16 qk-heads), m = 32768, r = 0.10 -> 3,277 tokens each
+    cu, _ = tail_seqlens([32768] * 36, 10, 100)
+    inp = synthetic.gdn_inputs(np.diff(cu.numpy()).tolist(), 16, 32, 128, 128, seed=21,
+                               backend="torch", device="cuda")
+    S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu)
+    torch.cuda.synchronize()
+    es, eo = _sampled_parity(inp, cu.numpy(), [0, 17, 35], [0, 1, 30, 31], 16, 32, S, o)
+    print("batched sampled: state %.3e output %.3e" % (es, eo), flush=True)
+    assert es <= STATE_TOL and eo <= OUT_TOL
+
+
+def test_varlen_full_size_sampled():
+    # 64 hits, m ~ U{4096..131072}, r = 0.05, 16 heads
+    m = synthetic.prefix_lengths(64, seed=5)
+    cu, _ = tail_seqlens(m, 5, 100)
+    lens = np.diff(cu.numpy())
+    inp = synthetic.gdn_inputs(lens.tolist(), 16, 16, 128, 128, seed=31, backend="torch", device="cuda")
+    S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu)
+    torch.cuda.synchronize()
+    seqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 13})
+    es, eo = _sampled_parity(inp, cu.numpy(), seqs, [0, 15], 16, 16, S, o)
+    print("varlen sampled: state %.3e output %.3e" % (es, eo), flush=True)
+    assert es <= STATE_TOL and eo <= OUT_TOL
+
+
+def test_packed_equals_separate_calls_bitwise():
+    lens = [70, 1, 129]
+    inp = synthetic.gdn_inputs(lens, 2, 4, 128, 128, seed=44).to("cuda")
+    S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    cu = inp.cu_seqlens.tolist()
+    for b, n in enumerate(lens):
+        sl = slice(cu[b], cu[b + 1])
+        Sb, ob = gdn_replay(inp.q[sl].contiguous(), inp.k[sl].contiguous(), inp.v[sl].contiguous(),
+                            inp.g[sl].contiguous(), inp.beta[sl].contiguous(), torch.tensor([0, n], dtype=torch.int32))
+        assert torch.equal(Sb[0], S[b])
+        assert torch.equal(ob, o[sl])
+
+
+def test_deterministic_and_state_only_and_in_place():
+    inp = synthetic.gdn_inputs([300, 97], 2, 4, 128, 128, seed=45).to("cuda")
+    S1, o1 = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    S2, o2 = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    assert torch.equal(S1, S2) and torch.equal(o1, o2)
+    S3, o3 = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, want_o=False)
+    assert o3 is None and torch.equal(S3, S1)
+    # state_in aliasing state_out: continue from S1 in place
+    ref, _ = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, state_in=S1.clone())
+    buf = S1.clone()
+    gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, state_in=buf, state_out=buf)
+    assert torch.equal(buf, ref)
+
+
+def test_beta_zero_is_pure_decay_on_gpu():
+    # beta = 0: S_m = e^{sum g} S_a and o_t = e^{gamma_t} S_a q_t, checked against the closed form
+    inp = synthetic.gdn_inputs([150], 1, 2, 128, 128, seed=46)
+    inp.beta.zero_()
+    rng = np.random.default_rng(1)
+    s_in = (rng.standard_normal((1, 2, 128, 128)) * 0.2).astype(np.float32)
+    d = inp.to("cuda")
+    S, o = gdn_replay(d.q, d.k, d.v, d.g, d.beta, inp.cu_seqlens, state_in=torch.from_numpy(s_in).cuda())
+    gam = np.cumsum(np64(inp.g), axis=0)
+    Sa = s_in.astype(np.float64)
+    for h in range(2):
+        assert rel(np64(S[0, h]), np.exp(gam[-1, h]) * Sa[0, h]) < 1e-5
+        expect = np.exp(gam[:, h])[:, None] * (np64(inp.q[:, 0]) @ Sa[0, h].T)
+        assert rel(np64(o[:, h]), expect) < OUT_TOL
+
+
+def test_split_call_matches_single_call():
+    inp = synthetic.gdn_inputs([333], 2, 2, 128, 128, seed=47).to("cuda")
+    S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
+    p = 100
+    S1, o1 = gdn_replay(inp.q[:p].contiguous(), inp.k[:p].contiguous(), inp.v[:p].contiguous(),
+                        inp.g[:p].contiguous(), inp.beta[:p].contiguous(), torch.tensor([0, p], dtype=torch.int32))
+    S2, o2 = gdn_replay(inp.q[p:].contiguous(), inp.k[p:].contiguous(), inp.v[p:].contiguous(),
+                        inp.g[p:].contiguous(), inp.beta[p:].contiguous(), torch.tensor([0, 333 - p], dtype=torch.int32),
+                        state_in=S1)
+    for h in range(2):
+        assert rel(np64(S2[0, h]), np64(S[0, h])) < STATE_TOL
+        assert rel(np64(torch.cat([o1, o2])[:, h]), np64(o[:, h])) < OUT_TOL
