@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the Tail-Replay state rebuild on one MI355X.
+
+A step is one pass of the replay hot path over one batch of synthetic inputs that are
+already resident in HBM: tail selection for every hit (k = ceil(r m)), then the
+library call(s) that rebuild the states.  Workloads:
+
+  group        12 groups x 3 LA layers, d_model 2048, 16 qk / 32 v heads, dk = dv = 128,
+               m = 32,768, r = 0.05 -> 1,639 tail tokens per group (tr_group_replay:
+               RMSNorm + projections, GDN recurrence, output projection + residual)
+  batched_r05  36 (group, layer) instances x 32 v-heads (16 qk), m = 32,768, r = 0.05
+  batched      the same at r = 0.10 (3,277 tokens)
+  single_hit   1 layer, 16 heads, m = 32,768, r = 0.05
+  varlen       64 hits, m ~ U{4096..131072}, r = 0.05, 16 heads
+
+Prints ONE JSON line.  The roofline entry covers the dominant kernel: its algorithmic
+bytes (or FLOPs) per launch divided by its average launch time, measured with HIP
+events on the stream the kernel runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "replayed token-heads/sec (GDN state rebuild)"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="group",
+                   choices=["group", "batched_r05", "batched", "single_hit", "varlen"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline sample time")
+    p.add_argument("--flush-cache", action="store_true",
+                   help="write 512 MiB between steps so no input is cache-resident (timed per launch)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------- counting rules
+def gdn_bytes(T, B, Hqk, Hv, dk, dv, with_o=True, with_state_in=False, elt=2):
+    """Algorithmic HBM bytes of one tr_gdn_replay launch: every input read once, every
+    output written once (q and k once per query/key head)."""
+    per_tok = Hqk * 2 * dk * elt + Hv * dv * elt + Hv * 8 + (Hv * dv * elt if with_o else 0)
+    state = B * Hv * dv * dk * 4 * (2 if with_state_in else 1)
+    return T * per_tok + state
+
+
+def gdn_useful_flops(lengths, Hv, dk, dv, C=64, with_o=True):
+    """Useful chunked-form FLOPs: per chunk of n tokens and value head, the dense products
+    K K^T, W = A(..)K, U = A(..)V, W S^T, the state update, and with outputs Q K^T, Q S^T, P U'."""
+    total = 0.0
+    for L in lengths:
+        full, rem = divmod(int(L), C)
+        for n in [C] * full + ([rem] if rem else []):
+            f = 2 * n * n * dk + 2 * n * n * dk + 2 * n * n * dv + 2 * n * dk * dv + 2 * dv * n * dk
+            if with_o:
+                f += 2 * n * n * dk + 2 * n * dk * dv + 2 * n * n * dv
+            total += f
+    return total * Hv
+
+
+def group_gemm_flops(G, L, n, d, Hqk, Hv, dk, dv):
+    proj = 2 * n * d * (2 * Hqk * dk + Hv * dv + 2 * Hv)
+    oproj = 2 * n * Hv * dv * d
+    return G * (L * proj + (L - 1) * oproj)
+
+
+# ---------------------------------------------------------------- workloads
+def build_workload(name, seed):
+    import torch
+    import synthetic
+    from linear_attention_state_amd import tail_seqlens
+
+    spec = dict(synthetic.WORKLOADS[name])
+    rn, rd = spec["r"]
+    if name == "group":
+        G, L = spec["G"], spec["L"]
+        ms = [spec["m"]] * G
+        cu, _ = tail_seqlens(ms, rn, rd)
+        n = int(cu[1])
+        gi = synthetic.group_inputs(G, L, n, spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"],
+                                    seed=seed, backend="torch", device="cuda")
+        return dict(kind="group", spec=spec, ms=ms, r=(rn, rd), n=n, inputs=gi)
+    if name == "varlen":
+        ms = synthetic.prefix_lengths(spec["n_hits"], seed=5 + seed)
+    else:
+        ms = [spec["m"]] * spec["B"]
+    cu, _ = tail_seqlens(ms, rn, rd)
+    lens = np.diff(cu.numpy()).tolist()
+    inp = synthetic.gdn_inputs(lens, spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"], seed=seed,
+                               backend="torch", device="cuda")
+    return dict(kind="gdn", spec=spec, ms=ms, r=(rn, rd), lens=lens, inputs=inp,
+                cu_dev=cu.to("cuda"))
+
+
+def make_step(w):
+    """Returns step() that runs tail selection + the replay call(s) on the current stream."""
+    import torch
+    from linear_attention_state_amd import GroupReplay, gdn_replay, tail_seqlens
+
+    rn, rd = w["r"]
+    if w["kind"] == "gdn":
+        inp, spec = w["inputs"], w["spec"]
+        B, Hv, dk, dv = len(w["lens"]), spec["Hv"], spec["dk"], spec["dv"]
+        S = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device="cuda")
+        o = torch.empty((inp.q.shape[0], Hv, dv), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            cu, _ = tail_seqlens(w["ms"], rn, rd)
+            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
+        return step, (S, o)
+    spec, gi = w["spec"], w["inputs"]
+    runner = GroupReplay(gi.weights, w["n"], spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+    states = torch.empty((spec["G"], spec["L"], spec["Hv"], spec["dv"], spec["dk"]), dtype=torch.float32,
+                         device="cuda")
+
+    def step():
+        tail_seqlens(w["ms"], rn, rd)
+        runner(gi.h_tail, states_out=states)
+    return step, (states,)
+
+
+def time_steps(step, steps, warmup, flush):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
+    if not flush:
+        t_host = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t_host) * 1e3
+        return e0.elapsed_time(e1) / steps, host_ms / steps, None
+    per = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    return float(np.mean(per)), None, per
+
+
+def time_launches(fn, steps, warmup):
+    """Average duration of one launch of fn() with HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(d)), float(np.median(d)), float(np.min(d))
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, min_seconds):
+    """The fp64 oracle on whole (sequence, all heads) units of the same workload until at
+    least min_seconds of CPU time has accumulated."""
+    import oracle
+
+    def np64(t):
+        return t.detach().to("cpu").double().numpy()
+
+    if w["kind"] == "gdn":
+        inp, spec = w["inputs"], w["spec"]
+        cu = np.concatenate([[0], np.cumsum(w["lens"])])
+        order = list(range(len(w["lens"])))
+        done_th, elapsed, units = 0, 0.0, 0
+        for b in order:
+            sl = slice(int(cu[b]), int(cu[b + 1]))
+            args = [np64(t[sl]) for t in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
+            t0 = time.perf_counter()
+            oracle.gdn(*args, [0, sl.stop - sl.start])
+            elapsed += time.perf_counter() - t0
+            done_th += (sl.stop - sl.start) * spec["Hv"]
+            units += 1
+            if elapsed >= min_seconds:
+                break
+        sample = "%d of %d sequences x %d heads (%d token-heads), fp64 token loop" % (
+            units, len(order), spec["Hv"], done_th)
+        return dict(value=done_th / elapsed, unit="token-heads/s", cores=oracle.num_threads(), kind="oracle",
+                    sample=sample, seconds=round(elapsed, 2))
+    # group: whole groups (all layers) through the chain oracle
+    spec, gi = w["spec"], w["inputs"]
+    done_th, elapsed, units = 0, 0.0, 0
+    for g in range(spec["G"]):
+        h = np64(gi.h_tail[g:g + 1])
+        ws = [[{k: np64(t) for k, t in d.items()} for d in gi.weights[g]]]
+        t0 = time.perf_counter()
+        oracle.group(h, ws, spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+        elapsed += time.perf_counter() - t0
+        done_th += w["n"] * spec["Hv"] * spec["L"]
+        units += 1
+        if elapsed >= min_seconds:
+            break
+    sample = "%d of %d groups x %d layers x %d heads x %d tokens, fp64" % (
+        units, spec["G"], spec["L"], spec["Hv"], w["n"])
+    return dict(value=done_th / elapsed, unit="token-heads/s", cores=oracle.num_threads(), kind="oracle",
+                sample=sample, seconds=round(elapsed, 2))
+
+
+# ---------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (the replay shards with no exchange "
+              "step; see the design notes); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import linear_attention_state_amd as tr
+    tr.lib()   # fails loudly if the HIP library is not built
+
+    w = build_workload(args.workload, args.seed)
+    step, outs = make_step(w)
+    ms, host_ms, per = time_steps(step, args.steps, args.warmup, args.flush_cache)
+    spec = w["spec"]
+
+    if w["kind"] == "gdn":
+        B, T = len(w["lens"]), int(sum(w["lens"]))
+        token_heads = T * spec["Hv"]
+        flops = gdn_useful_flops(w["lens"], spec["Hv"], spec["dk"], spec["dv"])
+        nbytes = gdn_bytes(T, B, spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+        inp = w["inputs"]
+        S, o = outs
+        from linear_attention_state_amd import gdn_replay
+        cu_host = torch.from_numpy(np.concatenate([[0], np.cumsum(w["lens"])]).astype(np.int32))
+
+        def kern():
+            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_host, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
+        k_mean, k_med, k_min = time_launches(kern, max(args.steps, 10), 2)
+        roof = dict(bound="hbm", achieved=nbytes / (k_mean * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                    traffic=None, kernel="gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"]),
+                    algorithmic_bytes=nbytes, avg_launch_us=k_mean * 1e3, median_launch_us=k_med * 1e3,
+                    min_launch_us=k_min * 1e3)
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        config = dict(workload=args.workload, hits=B, tokens_per_hit=(w["lens"][0] if len(set(w["lens"])) == 1
+                                                                   else "varlen"),
+                      total_tokens=T, Hqk=spec["Hqk"], Hv=spec["Hv"], dk=spec["dk"], dv=spec["dv"],
+                      r="%d/%d" % w["r"], chunk=64)
+        mfma = dict(useful_tflops=flops / (ms * 1e-3) / 1e12,
+                    frac_of_bf16_peak=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+    else:
+        G, L, n = spec["G"], spec["L"], w["n"]
+        token_heads = G * L * n * spec["Hv"]
+        gemm = group_gemm_flops(G, L, n, spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+        gdn_f = L * G * gdn_useful_flops([n], spec["Hv"], spec["dk"], spec["dv"])
+        flops = gemm + gdn_f
+        roof = group_roofline(w, args)
+        config = dict(workload=args.workload, groups=G, layers_per_group=L, tokens_per_group=n,
+                      d_model=spec["d_model"], Hqk=spec["Hqk"], Hv=spec["Hv"], dk=spec["dk"], dv=spec["dv"],
+                      r="%d/%d" % w["r"], chunk=64)
+        mfma = dict(useful_tflops=flops / (ms * 1e-3) / 1e12,
+                    frac_of_bf16_peak=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
+
+    line = {
+        "metric": METRIC,
+        "value": token_heads / (ms * 1e-3),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": roof,
+        "mfma": mfma,
+        "cache": "flushed before each step" if args.flush_cache else "warm (inputs resident in HBM)",
+    }
+    if host_ms is not None:
+        line["host_ms_per_step"] = host_ms
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, args.cpu_seconds)
+        cb["gpu_speedup"] = line["value"] / cb["value"]
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+def group_roofline(w, args):
+    raise NotImplementedError
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -49,6 +51,84 @@ tr_status finish_launch(hipError_t e, hipStream_t stream, const char* what) {
 }
 
 bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+typedef __bf16 bf16;
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of tr_group_replay: the running hidden x, the normalised y, q, k, v, g, beta, o.
+struct GroupLayout {
+    size_t x, y, q, k, v, o, g, beta, total;
+    GroupLayout(int32_t G, int32_t n, int32_t d, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv) {
+        const size_t rows = (size_t)G * n;
+        size_t off = 0;
+        auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes); return at; };
+        x = take(rows * d * 2);
+        y = take(rows * d * 2);
+        q = take(rows * Hqk * dk * 2);
+        k = take(rows * Hqk * dk * 2);
+        v = take(rows * Hv * dv * 2);
+        o = take(rows * Hv * dv * 2);
+        g = take(rows * Hv * 4);
+        beta = take(rows * Hv * 4);
+        total = off;
+    }
+};
+
+tr_status check_layer_dims(const char* fn, int32_t G, int32_t L, int32_t n, int32_t d, int32_t Hqk, int32_t Hv,
+                           int32_t dk, int32_t dv, float eps) {
+    if (G < 1 || L < 1 || n < 1) return fail(TR_ERR_INVALID_ARG, "%s: need G, L, n_tokens >= 1", fn);
+    if (Hqk < 1 || Hv < 1 || Hv % Hqk != 0)
+        return fail(TR_ERR_INVALID_ARG, "%s: need Hv a positive multiple of Hqk (Hqk=%d, Hv=%d)", fn, Hqk, Hv);
+    if (dk != 128 || dv != 128) return fail(TR_ERR_UNSUPPORTED, "%s: the layer path supports dk = dv = 128", fn);
+    if (d < 128 || d % 128 != 0) return fail(TR_ERR_UNSUPPORTED, "%s: d_model must be a multiple of 128", fn);
+    if (Hv > 64) return fail(TR_ERR_UNSUPPORTED, "%s: Hv <= 64 supported", fn);
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(TR_ERR_INVALID_ARG, "%s: rms_eps must be finite and >= 0", fn);
+    if ((int64_t)G * n > INT32_MAX / 64) return fail(TR_ERR_INVALID_ARG, "%s: too many tokens", fn);
+    return TR_OK;
+}
+
+tr_status check_weights(const char* fn, const tr_la_weights* w, bool need_o, int gi, int li) {
+    if (!w->w_qk || !w->w_v || !w->w_a || !w->w_b || (need_o && !w->w_o))
+        return fail(TR_ERR_INVALID_ARG, "%s: null weight pointer (group %d, layer %d)", fn, gi, li);
+    return TR_OK;
+}
+
+// Projections for G blocks; weights of block g are wp[g * stride + offset].
+hipError_t layer_inputs(const void* x, const tr_la_weights* const* wp, int stride, int offset, int G, int n, int d,
+                        int Hqk, int Hv, float eps, bf16* y, bf16* q, bf16* k, bf16* v, float* g, float* beta,
+                        hipStream_t s) {
+    for (int g0 = 0; g0 < G; g0 += tr::kMaxGroupsPerLaunch) {
+        const int gb = std::min(tr::kMaxGroupsPerLaunch, G - g0);
+        tr::PtrTable gain{}, wqk{}, wv{}, wa{}, wb{};
+        for (int i = 0; i < gb; ++i) {
+            const tr_la_weights* w = wp[(size_t)(g0 + i) * stride + offset];
+            gain.p[i] = w->rms_gain; wqk.p[i] = w->w_qk; wv.p[i] = w->w_v; wa.p[i] = w->w_a; wb.p[i] = w->w_b;
+        }
+        const size_t r0 = (size_t)g0 * n;
+        hipError_t e = tr::launch_rmsnorm((const bf16*)x + r0 * d, y + r0 * d, gain, gb, n, d, eps, s);
+        if (e != hipSuccess) return e;
+        e = tr::launch_layer_in_gemm(y + r0 * d, wqk, wv, wa, wb, gb, n, d, Hqk, Hv,
+                                     q + r0 * Hqk * 128, k + r0 * Hqk * 128, v + r0 * Hv * 128,
+                                     g + r0 * Hv, beta + r0 * Hv, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t output_residual(const void* x_in, const void* o, const tr_la_weights* const* wp, int stride, int offset,
+                           int G, int n, int d, int din, void* x_out, hipStream_t s) {
+    for (int g0 = 0; g0 < G; g0 += tr::kMaxGroupsPerLaunch) {
+        const int gb = std::min(tr::kMaxGroupsPerLaunch, G - g0);
+        tr::PtrTable wo{};
+        for (int i = 0; i < gb; ++i) wo.p[i] = wp[(size_t)(g0 + i) * stride + offset]->w_o;
+        const size_t r0 = (size_t)g0 * n;
+        hipError_t e = tr::launch_out_residual_gemm((const bf16*)o + r0 * din, wo, gb, n, din, d,
+                                                    (const bf16*)x_in + r0 * d, (bf16*)x_out + r0 * d, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -127,34 +207,120 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens_dev;
     a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = q_scale;
     a.state_in = state_in; a.state_out = state_out; a.o = o; a.max_len = max_len;
+    a.uniform_len = 0; a.state_bstride = (int64_t)Hv * dv * dk;
     hipStream_t s = (hipStream_t)stream;
     const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_chunk_bf16(a, s) : tr::launch_gdn_token_f32(a, s);
     return finish_launch(e, s, fn);
 }
 
 size_t tr_la_layer_inputs_workspace_size(int32_t G, int32_t n_tokens, int32_t d_model) {
-    if (G < 1 || n_tokens < 0 || d_model < 1) return 0;
-    return (size_t)G * n_tokens * d_model * 2;
+    if (G < 1 || n_tokens < 1 || d_model < 1) return 0;
+    return align_up((size_t)G * n_tokens * d_model * 2);
 }
 
-tr_status tr_la_layer_inputs(const void*, const tr_la_weights* const*, int32_t, int32_t, int32_t,
-                             int32_t, int32_t, int32_t, int32_t, float, void*, void*, void*, float*, float*,
-                             void*, size_t, void*) {
-    return fail(TR_ERR_UNSUPPORTED, "tr_la_layer_inputs: not available in this build");
+tr_status tr_la_layer_inputs(const void* x, const tr_la_weights* const* w,
+                             int32_t G, int32_t n_tokens, int32_t d_model,
+                             int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, float rms_eps,
+                             void* q, void* k, void* v, float* g_out, float* beta_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "tr_la_layer_inputs";
+    tr_status st = check_layer_dims(fn, G, 1, n_tokens, d_model, Hqk, Hv, dk, dv, rms_eps);
+    if (st != TR_OK) return st;
+    if (!x || !w || !q || !k || !v || !g_out || !beta_out) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (int32_t gi = 0; gi < G; ++gi) {
+        if (!w[gi]) return fail(TR_ERR_INVALID_ARG, "%s: null weights for block %d", fn, gi);
+        st = check_weights(fn, w[gi], false, gi, 0);
+        if (st != TR_OK) return st;
+    }
+    const size_t need = tr_la_layer_inputs_workspace_size(G, n_tokens, d_model);
+    if (!workspace || workspace_bytes < need)
+        return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    return finish_launch(layer_inputs(x, w, 1, 0, G, n_tokens, d_model, Hqk, Hv, rms_eps, (bf16*)workspace,
+                                      (bf16*)q, (bf16*)k, (bf16*)v, g_out, beta_out, s), s, fn);
 }
 
-tr_status tr_la_output_residual(const void*, const void*, const tr_la_weights* const*, int32_t, int32_t,
-                                int32_t, int32_t, int32_t, void*, void*) {
-    return fail(TR_ERR_UNSUPPORTED, "tr_la_output_residual: not available in this build");
+tr_status tr_la_output_residual(const void* x_in, const void* o, const tr_la_weights* const* w,
+                                int32_t G, int32_t n_tokens, int32_t d_model, int32_t Hv, int32_t dv,
+                                void* x_out, void* stream) {
+    static const char* fn = "tr_la_output_residual";
+    if (G < 1 || n_tokens < 1) return fail(TR_ERR_INVALID_ARG, "%s: need G >= 1 and n_tokens >= 1", fn);
+    if (d_model < 128 || d_model % 128 != 0) return fail(TR_ERR_UNSUPPORTED, "%s: d_model must be a multiple of 128", fn);
+    if (Hv < 1 || dv < 1 || ((int64_t)Hv * dv) % 64 != 0)
+        return fail(TR_ERR_UNSUPPORTED, "%s: Hv * dv must be a positive multiple of 64", fn);
+    if (!x_in || !o || !w || !x_out) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (int32_t gi = 0; gi < G; ++gi)
+        if (!w[gi] || !w[gi]->w_o) return fail(TR_ERR_INVALID_ARG, "%s: null w_o for block %d", fn, gi);
+    hipStream_t s = (hipStream_t)stream;
+    return finish_launch(output_residual(x_in, o, w, 1, 0, G, n_tokens, d_model, Hv * dv, x_out, s), s, fn);
 }
 
-size_t tr_group_replay_workspace_size(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t) {
-    return 0;
+size_t tr_group_replay_workspace_size(int32_t G, int32_t L, int32_t n_tokens, int32_t d_model,
+                                      int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv) {
+    if (G < 1 || L < 1 || n_tokens < 1 || d_model < 1 || Hqk < 1 || Hv < 1 || dk < 1 || dv < 1) return 0;
+    return GroupLayout(G, n_tokens, d_model, Hqk, Hv, dk, dv).total;
 }
 
-tr_status tr_group_replay(const void*, const tr_la_weights*, int32_t, int32_t, int32_t, int32_t,
-                          int32_t, int32_t, int32_t, int32_t, float, float*, void*, size_t, void*) {
-    return fail(TR_ERR_UNSUPPORTED, "tr_group_replay: not available in this build");
+tr_status tr_group_replay(const void* h_tail, const tr_la_weights* w,
+                          int32_t G, int32_t L, int32_t n_tokens, int32_t d_model,
+                          int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, float rms_eps,
+                          float* states_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    static const char* fn = "tr_group_replay";
+    tr_status st = check_layer_dims(fn, G, L, n_tokens, d_model, Hqk, Hv, dk, dv, rms_eps);
+    if (st != TR_OK) return st;
+    if (!h_tail || !w || !states_out) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (int32_t gi = 0; gi < G; ++gi)
+        for (int32_t li = 0; li < L; ++li) {
+            st = check_weights(fn, &w[(size_t)gi * L + li], li < L - 1, gi, li);
+            if (st != TR_OK) return st;
+        }
+    const GroupLayout lay(G, n_tokens, d_model, Hqk, Hv, dk, dv);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, lay.total);
+
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char* ws = (unsigned char*)workspace;
+    bf16* xbuf = (bf16*)(ws + lay.x);
+    bf16* ybuf = (bf16*)(ws + lay.y);
+    bf16* qbuf = (bf16*)(ws + lay.q);
+    bf16* kbuf = (bf16*)(ws + lay.k);
+    bf16* vbuf = (bf16*)(ws + lay.v);
+    bf16* obuf = (bf16*)(ws + lay.o);
+    float* gbuf = (float*)(ws + lay.g);
+    float* bbuf = (float*)(ws + lay.beta);
+    std::vector<const tr_la_weights*> wp((size_t)G * L);
+    for (size_t i = 0; i < wp.size(); ++i) wp[i] = &w[i];
+
+    const int64_t state_elems = (int64_t)Hv * dv * dk;
+    const void* x_cur = h_tail;
+    for (int32_t li = 0; li < L; ++li) {
+        const bool last = li == L - 1;
+        // projections in front of the recurrence (stride L through the weight table)
+        hipError_t e = layer_inputs(x_cur, wp.data(), L, li, G, n_tokens, d_model, Hqk, Hv, rms_eps, ybuf,
+                                    qbuf, kbuf, vbuf, gbuf, bbuf, s);
+        if (e != hipSuccess) return finish_launch(e, s, fn);
+        // the recurrence from the zero state; the last layer keeps its state only
+        tr::GdnArgs a;
+        a.q = qbuf; a.k = kbuf; a.v = vbuf; a.g = gbuf; a.beta = bbuf;
+        a.cu_seqlens = nullptr; a.uniform_len = n_tokens;
+        a.B = G; a.T = G * n_tokens; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = 1.0f;
+        a.state_in = nullptr; a.state_out = states_out + (int64_t)li * state_elems;
+        a.state_bstride = (int64_t)L * state_elems;
+        a.o = last ? nullptr : obuf; a.max_len = n_tokens;
+        e = tr::launch_gdn_chunk_bf16(a, s);
+        if (e != hipSuccess) return finish_launch(e, s, fn);
+        if (!last) {
+            e = output_residual(x_cur, obuf, wp.data(), L, li, G, n_tokens, d_model, Hv * dv, xbuf, s);
+            if (e != hipSuccess) return finish_launch(e, s, fn);
+            x_cur = xbuf;
+        }
+        if (debug_sync()) {
+            const tr_status ds = finish_launch(hipSuccess, s, fn);
+            if (ds != TR_OK) return ds;
+        }
+    }
+    return finish_launch(hipSuccess, s, fn);
 }
 
 }  // extern "C"

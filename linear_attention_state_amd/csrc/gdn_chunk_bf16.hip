@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(DV * 2, 1)
 gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
-                      int B, int Hqk, int Hv, float q_scale,
+                      int B, int Hqk, int Hv, float q_scale, int uniform_len, long long state_bstride,
                       const float* state_in, float* state_out, bf16* __restrict__ o)
 {
     constexpr int NW = DV / 32;            // waves; wave w owns dv columns [32w, 32w+32)
@@ -137,15 +137,15 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int b = blockIdx.x / Hv;
     const int hv = blockIdx.x % Hv;
     const int hq = hv / (Hv / Hqk);
-    const int bos = cu[b];
-    const int len = cu[b + 1] - bos;
+    const int bos = cu ? cu[b] : b * uniform_len;
+    const int len = cu ? cu[b + 1] - bos : uniform_len;
     const int n_chunks = (len + CH - 1) / CH;
     const int col0 = 32 * wave;            // this wave's first dv column
 
     // ---- state: S^T tiles, tile r covers dk rows [32r, 32r+32), columns = own dv cols
     f32x16 St[KT_TILES];
     {
-        const size_t base = ((size_t)b * Hv + hv) * DV * DK;
+        const size_t base = (size_t)b * state_bstride + (size_t)hv * DV * DK;
 #pragma unroll
         for (int r = 0; r < KT_TILES; ++r) {
             if (state_in) {
@@ -442,7 +442,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     // ---- write the final state
     {
-        const size_t base = ((size_t)b * Hv + hv) * DV * DK;
+        const size_t base = (size_t)b * state_bstride + (size_t)hv * DV * DK;
 #pragma unroll
         for (int r = 0; r < KT_TILES; ++r) {
 #pragma unroll
@@ -467,7 +467,8 @@ hipError_t launch(const GdnArgs& a, hipStream_t stream) {
     const dim3 block(DV * 2);
     hipLaunchKernelGGL(kern, grid, block, smem, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
-                       a.B, a.Hqk, a.Hv, a.q_scale, a.state_in, a.state_out, (bf16*)a.o);
+                       a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
+                       a.state_in, a.state_out, (bf16*)a.o);
     return hipGetLastError();
 }
 

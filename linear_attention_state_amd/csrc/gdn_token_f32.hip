@@ -21,7 +21,7 @@ __global__ void __launch_bounds__(128)
 gdn_token_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                      const float* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
-                     int Hqk, int Hv, int DV, float q_scale,
+                     int Hqk, int Hv, int DV, float q_scale, int uniform_len, long long state_bstride,
                      const float* state_in, float* state_out, float* __restrict__ o)
 {
     __shared__ float sK[CH][DK];
@@ -33,9 +33,9 @@ gdn_token_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int hv = blockIdx.x % Hv;
     const int hq = hv / (Hv / Hqk);
     const int r = threadIdx.x;            // state row (value index); blockDim.x == DV
-    const int bos = cu[b];
-    const int len = cu[b + 1] - bos;
-    const size_t sbase = (((size_t)b * Hv + hv) * DV + r) * DK;
+    const int bos = cu ? cu[b] : b * uniform_len;
+    const int len = cu ? cu[b + 1] - bos : uniform_len;
+    const size_t sbase = (size_t)b * state_bstride + ((size_t)hv * DV + r) * DK;
 
     float S[DK];
 #pragma unroll
@@ -83,11 +83,13 @@ hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream) {
     if (a.dk == 128) {
         hipLaunchKernelGGL(gdn_token_f32_kernel<128>, grid, block, 0, stream,
                            (const float*)a.q, (const float*)a.k, (const float*)a.v, a.g, a.beta,
-                           a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.state_in, a.state_out, (float*)a.o);
+                           a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
+                           a.state_in, a.state_out, (float*)a.o);
     } else if (a.dk == 64) {
         hipLaunchKernelGGL(gdn_token_f32_kernel<64>, grid, block, 0, stream,
                            (const float*)a.q, (const float*)a.k, (const float*)a.v, a.g, a.beta,
-                           a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.state_in, a.state_out, (float*)a.o);
+                           a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
+                           a.state_in, a.state_out, (float*)a.o);
     } else {
         return hipErrorInvalidValue;
     }

@@ -14,7 +14,9 @@ struct GdnArgs {
     const void* v;
     const float* g;
     const float* beta;
-    const int32_t* cu_seqlens;   // device
+    const int32_t* cu_seqlens;   // device, or null: every sequence has uniform_len tokens
+    int32_t uniform_len;
+    int64_t state_bstride;       // elements between sequences in state_in / state_out
     int32_t B, T, Hqk, Hv, dk, dv;
     float q_scale;
     const float* state_in;       // may be null (zero state)
@@ -28,28 +30,17 @@ hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream);
 // Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
 hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream);
 
-// Group path (la_layer.hip).
-struct LayerInputsArgs {
-    const void* x;               // [G, n, d] bf16
-    const void* const* w_qk;     // device array of G pointers
-    const void* const* w_v;
-    const void* const* w_a;
-    const void* const* w_b;
-    const void* const* gain;     // entries may be null
-    int32_t G, n, d, Hqk, Hv, dk, dv;
-    float rms_eps;
-    void* q; void* k; void* v; float* g; float* beta;
-    void* y;                     // workspace: [G, n, d] bf16 normalised hidden
+// Group path (la_layer.hip).  Per-group weight pointers travel in kernel arguments.
+constexpr int kMaxGroupsPerLaunch = 16;
+struct PtrTable {
+    const void* p[kMaxGroupsPerLaunch];
 };
-hipError_t launch_la_layer_inputs(const LayerInputsArgs& a, hipStream_t stream);
-
-struct OutResArgs {
-    const void* x_in;            // [G, n, d] bf16
-    const void* o;               // [G*n, Hv*dv] bf16
-    const void* const* w_o;      // device array of G pointers
-    int32_t G, n, d, din;
-    void* x_out;
-};
-hipError_t launch_la_output_residual(const OutResArgs& a, hipStream_t stream);
+hipError_t launch_rmsnorm(const __bf16* x, __bf16* y, const PtrTable& gain, int G, int n, int d, float eps,
+                          hipStream_t stream);
+hipError_t launch_layer_in_gemm(const __bf16* y, const PtrTable& w_qk, const PtrTable& w_v, const PtrTable& w_a,
+                                const PtrTable& w_b, int G, int n, int d, int Hqk, int Hv,
+                                __bf16* q, __bf16* k, __bf16* v, float* g, float* beta, hipStream_t stream);
+hipError_t launch_out_residual_gemm(const __bf16* o, const PtrTable& w_o, int G, int n, int din, int d,
+                                    const __bf16* x_in, __bf16* x_out, hipStream_t stream);
 
 }  // namespace tr
