@@ -308,7 +308,67 @@ def main():
 
 
 def group_roofline(w, args):
-    raise NotImplementedError
+    """Time every kernel of the group step through its own entry point, in the step's launch
+    configuration, and return the roofline entry of the one with the largest per-step time."""
+    import torch
+    from linear_attention_state_amd import gdn_replay, la_output_residual, la_project, rmsnorm
+
+    spec, gi = w["spec"], w["inputs"]
+    G, L, n, d = spec["G"], spec["L"], w["n"], spec["d_model"]
+    Hqk, Hv, dk, dv = spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"]
+    reps = max(args.steps, 10)
+    ws0 = [gi.weights[g][0] for g in range(G)]
+    x = gi.h_tail
+    y = torch.empty_like(x)
+    t_norm = time_launches(lambda: rmsnorm(x, [None] * G, y=y), reps, 2)
+    out = la_project(y, ws0, Hqk, Hv, dk, dv)
+    t_proj = time_launches(lambda: la_project(y, ws0, Hqk, Hv, dk, dv, out=out), reps, 2)
+    q, k, v, g, beta = out
+    cu = torch.arange(G + 1, dtype=torch.int32) * n
+    cu_dev = cu.to("cuda")
+    S = torch.empty((G, Hv, dv, dk), dtype=torch.float32, device="cuda")
+    o = torch.empty((G * n, Hv, dv), dtype=torch.bfloat16, device="cuda")
+    t_gdn_o = time_launches(lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S, o=o), reps, 2)
+    t_gdn_s = time_launches(lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S,
+                                               want_o=False), reps, 2)
+    xo = torch.empty_like(x)
+    o2 = o.view(G * n, Hv * dv)
+    t_out = time_launches(lambda: la_output_residual(x, o2, ws0, Hv, dv, x_out=xo), reps, 2)
+
+    proj_flops = 2.0 * G * n * d * (2 * Hqk * dk + Hv * dv + 2 * Hv)
+    out_flops = 2.0 * G * n * Hv * dv * d
+    gdn_o_bytes = gdn_bytes(G * n, G, Hqk, Hv, dk, dv, with_o=True)
+    gdn_s_bytes = gdn_bytes(G * n, G, Hqk, Hv, dk, dv, with_o=False)
+    norm_bytes = 2.0 * G * n * d * 2
+    kernels = {
+        "gemm_tn_kernel<layer_in> (RMSNorm'd hidden x [W_qk|W_v|W_a|W_b]^T, fused L2 norm / gates)":
+            dict(avg_us=t_proj[0] * 1e3, per_step=L, bound="mfma", work=proj_flops),
+        "gdn_chunk_bf16_kernel<128,128> (with outputs)":
+            dict(avg_us=t_gdn_o[0] * 1e3, per_step=L - 1, bound="hbm", work=gdn_o_bytes),
+        "gdn_chunk_bf16_kernel<128,128> (state only)":
+            dict(avg_us=t_gdn_s[0] * 1e3, per_step=1, bound="hbm", work=gdn_s_bytes),
+        "gemm_tn_kernel<residual> (o W_o^T + x)":
+            dict(avg_us=t_out[0] * 1e3, per_step=L - 1, bound="mfma", work=out_flops),
+        "rmsnorm_kernel":
+            dict(avg_us=t_norm[0] * 1e3, per_step=L, bound="hbm", work=norm_bytes),
+    }
+    for kd in kernels.values():
+        kd["us_per_step"] = kd["avg_us"] * kd["per_step"]
+        if kd["bound"] == "mfma":
+            kd["achieved_tflops"] = kd["work"] / (kd["avg_us"] * 1e-6) / 1e12
+        else:
+            kd["achieved_gbs"] = kd["work"] / (kd["avg_us"] * 1e-6) / 1e9
+    name, top = max(kernels.items(), key=lambda kv: kv[1]["us_per_step"])
+    if top["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=top["achieved_tflops"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    algorithmic_flops=top["work"])
+    else:
+        roof = dict(bound="hbm", achieved=top["achieved_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    algorithmic_bytes=top["work"])
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel=name, avg_launch_us=top["avg_us"],
+                kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()
+                             if kk != "work"} for k, v in kernels.items()})
+    return roof
 
 
 if __name__ == "__main__":

@@ -159,6 +159,25 @@ tr_status tr_la_layer_inputs(const void* x, const tr_la_weights* const* w,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * The two halves of tr_la_layer_inputs, each a single kernel:
+ *
+ * tr_rmsnorm: y = bf16( x / sqrt(mean(x^2) + rms_eps) * gain ) row by row for G blocks of
+ *   n_tokens rows; gain[g] is block g's [d_model] bf16 gain or NULL (unit gain).
+ *   x, y [device] [G, n_tokens, d_model] bf16 (may be the same buffer); gain [host] array
+ *   of G device pointers.  Supported: d_model % 128 == 0.
+ *
+ * tr_la_project: q, k, v, g, beta from an already normalised y (the projection GEMM with
+ *   the per-head L2 norm and gate epilogue of tr_la_layer_inputs).  Same arguments and
+ *   layouts as tr_la_layer_inputs, without the workspace.
+ * ------------------------------------------------------------------------------- */
+tr_status tr_rmsnorm(const void* x, const void* const* gain, int32_t G, int32_t n_tokens, int32_t d_model,
+                     float rms_eps, void* y, void* stream);
+tr_status tr_la_project(const void* y, const tr_la_weights* const* w,
+                        int32_t G, int32_t n_tokens, int32_t d_model,
+                        int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                        void* q, void* k, void* v, float* g_out, float* beta_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * tr_la_output_residual -- x_out = bf16( x_in + o Wo^T ) for G blocks with their own
  * Wo (the LA layer's output projection and residual, in front of the next LA layer
  * of the group).

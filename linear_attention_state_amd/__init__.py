@@ -5,8 +5,8 @@ this package is its thin Python binding.  Importing the package does not load th
 library; the first call does, and fails loudly if it has not been built.
 """
 from .ops import (GroupReplay, gdn_replay, group_replay, la_layer_inputs,  # noqa: F401
-                  la_output_residual, tail_length, tail_seqlens)
+                  la_output_residual, la_project, rmsnorm, tail_length, tail_seqlens)
 from ._lib import LIB_PATH, TailReplayError, lib  # noqa: F401
 
-__all__ = ["gdn_replay", "group_replay", "GroupReplay", "la_layer_inputs", "la_output_residual",
+__all__ = ["gdn_replay", "group_replay", "GroupReplay", "la_layer_inputs", "la_output_residual", "la_project", "rmsnorm",
            "tail_length", "tail_seqlens", "TailReplayError", "lib", "LIB_PATH"]

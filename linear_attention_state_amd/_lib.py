@@ -38,6 +38,9 @@ SIGNATURES = {
     "tr_la_layer_inputs_workspace_size": (_sz, [_i32, _i32, _i32]),
     "tr_la_layer_inputs": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tr_rmsnorm": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _f32, _vp, _vp]),
+    "tr_la_project": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _vp, _vp, _vp, _vp, _vp, _vp]),
     "tr_la_output_residual": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "tr_group_replay_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "tr_group_replay": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,

@@ -94,26 +94,38 @@ tr_status check_weights(const char* fn, const tr_la_weights* w, bool need_o, int
     return TR_OK;
 }
 
-// Projections for G blocks; weights of block g are wp[g * stride + offset].
+// Projection GEMM for G blocks; weights of block g are wp[g * stride + offset].
+hipError_t project(const void* y, const tr_la_weights* const* wp, int stride, int offset, int G, int n, int d,
+                   int Hqk, int Hv, bf16* q, bf16* k, bf16* v, float* g, float* beta, hipStream_t s) {
+    for (int g0 = 0; g0 < G; g0 += tr::kMaxGroupsPerLaunch) {
+        const int gb = std::min(tr::kMaxGroupsPerLaunch, G - g0);
+        tr::PtrTable wqk{}, wv{}, wa{}, wb{};
+        for (int i = 0; i < gb; ++i) {
+            const tr_la_weights* w = wp[(size_t)(g0 + i) * stride + offset];
+            wqk.p[i] = w->w_qk; wv.p[i] = w->w_v; wa.p[i] = w->w_a; wb.p[i] = w->w_b;
+        }
+        const size_t r0 = (size_t)g0 * n;
+        const hipError_t e = tr::launch_layer_in_gemm((const bf16*)y + r0 * d, wqk, wv, wa, wb, gb, n, d, Hqk, Hv,
+                                                      q + r0 * Hqk * 128, k + r0 * Hqk * 128, v + r0 * Hv * 128,
+                                                      g + r0 * Hv, beta + r0 * Hv, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// RMSNorm then projections for G blocks (y is scratch of [G, n, d] bf16).
 hipError_t layer_inputs(const void* x, const tr_la_weights* const* wp, int stride, int offset, int G, int n, int d,
                         int Hqk, int Hv, float eps, bf16* y, bf16* q, bf16* k, bf16* v, float* g, float* beta,
                         hipStream_t s) {
     for (int g0 = 0; g0 < G; g0 += tr::kMaxGroupsPerLaunch) {
         const int gb = std::min(tr::kMaxGroupsPerLaunch, G - g0);
-        tr::PtrTable gain{}, wqk{}, wv{}, wa{}, wb{};
-        for (int i = 0; i < gb; ++i) {
-            const tr_la_weights* w = wp[(size_t)(g0 + i) * stride + offset];
-            gain.p[i] = w->rms_gain; wqk.p[i] = w->w_qk; wv.p[i] = w->w_v; wa.p[i] = w->w_a; wb.p[i] = w->w_b;
-        }
-        const size_t r0 = (size_t)g0 * n;
-        hipError_t e = tr::launch_rmsnorm((const bf16*)x + r0 * d, y + r0 * d, gain, gb, n, d, eps, s);
-        if (e != hipSuccess) return e;
-        e = tr::launch_layer_in_gemm(y + r0 * d, wqk, wv, wa, wb, gb, n, d, Hqk, Hv,
-                                     q + r0 * Hqk * 128, k + r0 * Hqk * 128, v + r0 * Hv * 128,
-                                     g + r0 * Hv, beta + r0 * Hv, s);
+        tr::PtrTable gain{};
+        for (int i = 0; i < gb; ++i) gain.p[i] = wp[(size_t)(g0 + i) * stride + offset]->rms_gain;
+        const size_t r0 = (size_t)g0 * n * d;
+        const hipError_t e = tr::launch_rmsnorm((const bf16*)x + r0, y + r0, gain, gb, n, d, eps, s);
         if (e != hipSuccess) return e;
     }
-    return hipSuccess;
+    return project(y, wp, stride, offset, G, n, d, Hqk, Hv, q, k, v, g, beta, s);
 }
 
 hipError_t output_residual(const void* x_in, const void* o, const tr_la_weights* const* wp, int stride, int offset,
@@ -253,6 +265,44 @@ tr_status tr_la_output_residual(const void* x_in, const void* o, const tr_la_wei
         if (!w[gi] || !w[gi]->w_o) return fail(TR_ERR_INVALID_ARG, "%s: null w_o for block %d", fn, gi);
     hipStream_t s = (hipStream_t)stream;
     return finish_launch(output_residual(x_in, o, w, 1, 0, G, n_tokens, d_model, Hv * dv, x_out, s), s, fn);
+}
+
+tr_status tr_rmsnorm(const void* x, const void* const* gain, int32_t G, int32_t n_tokens, int32_t d_model,
+                     float rms_eps, void* y, void* stream) {
+    static const char* fn = "tr_rmsnorm";
+    if (G < 1 || n_tokens < 1) return fail(TR_ERR_INVALID_ARG, "%s: need G >= 1 and n_tokens >= 1", fn);
+    if (d_model < 128 || d_model % 128 != 0) return fail(TR_ERR_UNSUPPORTED, "%s: d_model must be a multiple of 128", fn);
+    if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps)) return fail(TR_ERR_INVALID_ARG, "%s: rms_eps must be finite and >= 0", fn);
+    if (!x || !y || !gain) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    hipStream_t s = (hipStream_t)stream;
+    for (int g0 = 0; g0 < G; g0 += tr::kMaxGroupsPerLaunch) {
+        const int gb = std::min(tr::kMaxGroupsPerLaunch, G - g0);
+        tr::PtrTable gt{};
+        for (int i = 0; i < gb; ++i) gt.p[i] = gain[g0 + i];
+        const size_t r0 = (size_t)g0 * n_tokens * d_model;
+        const hipError_t e = tr::launch_rmsnorm((const bf16*)x + r0, (bf16*)y + r0, gt, gb, n_tokens, d_model,
+                                                rms_eps, s);
+        if (e != hipSuccess) return finish_launch(e, s, fn);
+    }
+    return finish_launch(hipSuccess, s, fn);
+}
+
+tr_status tr_la_project(const void* y, const tr_la_weights* const* w,
+                        int32_t G, int32_t n_tokens, int32_t d_model,
+                        int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                        void* q, void* k, void* v, float* g_out, float* beta_out, void* stream) {
+    static const char* fn = "tr_la_project";
+    tr_status st = check_layer_dims(fn, G, 1, n_tokens, d_model, Hqk, Hv, dk, dv, 0.f);
+    if (st != TR_OK) return st;
+    if (!y || !w || !q || !k || !v || !g_out || !beta_out) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (int32_t gi = 0; gi < G; ++gi) {
+        if (!w[gi]) return fail(TR_ERR_INVALID_ARG, "%s: null weights for block %d", fn, gi);
+        st = check_weights(fn, w[gi], false, gi, 0);
+        if (st != TR_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    return finish_launch(project(y, w, 1, 0, G, n_tokens, d_model, Hqk, Hv, (bf16*)q, (bf16*)k, (bf16*)v,
+                                 g_out, beta_out, s), s, fn);
 }
 
 size_t tr_group_replay_workspace_size(int32_t G, int32_t L, int32_t n_tokens, int32_t d_model,

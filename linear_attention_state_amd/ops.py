@@ -131,6 +131,44 @@ def la_layer_inputs(x, weights: Sequence[dict], Hqk, Hv, dk, dv, rms_eps=1e-6, s
     return q, k, v, g, beta
 
 
+def rmsnorm(x, gains: Sequence, rms_eps=1e-6, y=None, stream=None):
+    """y = bf16(x / sqrt(mean(x^2) + eps) * gain) per block (tr_rmsnorm); gains: G tensors or None."""
+    _need(x.is_cuda and x.dtype == torch.bfloat16 and x.is_contiguous() and x.dim() == 3, "x: [G, n, d] bf16")
+    G, n, d = x.shape
+    _need(len(gains) == G, "one gain (or None) per block")
+    for t in gains:
+        if t is not None:
+            _need(t.is_cuda and t.dtype == torch.bfloat16 and t.numel() == d, "gain must be bf16 [d_model]")
+    if y is None:
+        y = torch.empty_like(x)
+    arr = (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else None for t in gains])
+    check(lib().tr_rmsnorm(_ptr(x), ctypes.cast(arr, ctypes.c_void_p), G, n, d, float(rms_eps), _ptr(y),
+                           _stream(stream)))
+    return y
+
+
+def la_project(y, weights: Sequence[dict], Hqk, Hv, dk, dv, out=None, stream=None):
+    """q, k, v, g, beta from a normalised hidden y [G, n, d] (tr_la_project)."""
+    _need(y.is_cuda and y.dtype == torch.bfloat16 and y.is_contiguous() and y.dim() == 3, "y: [G, n, d] bf16")
+    G, n, d = y.shape
+    _need(len(weights) == G, "one weight set per block")
+    for w in weights:
+        _check_weights(w, d, Hqk, Hv, dk, dv, need_o=False)
+    dev = y.device
+    if out is None:
+        out = (torch.empty((G * n, Hqk, dk), dtype=torch.bfloat16, device=dev),
+               torch.empty((G * n, Hqk, dk), dtype=torch.bfloat16, device=dev),
+               torch.empty((G * n, Hv, dv), dtype=torch.bfloat16, device=dev),
+               torch.empty((G * n, Hv), dtype=torch.float32, device=dev),
+               torch.empty((G * n, Hv), dtype=torch.float32, device=dev))
+    q, k, v, g, beta = out
+    structs = [_weights_struct(w) for w in weights]
+    arr = (ctypes.POINTER(LaWeights) * G)(*[ctypes.pointer(s) for s in structs])
+    check(lib().tr_la_project(_ptr(y), ctypes.cast(arr, ctypes.c_void_p), G, n, d, Hqk, Hv, dk, dv,
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _stream(stream)))
+    return out
+
+
 def la_output_residual(x_in, o, weights: Sequence[dict], Hv, dv, x_out=None, stream=None):
     """x_out = bf16(x_in + o Wo^T) per block (tr_la_output_residual)."""
     _need(x_in.is_cuda and x_in.dtype == torch.bfloat16 and x_in.is_contiguous() and x_in.dim() == 3, "x_in")
