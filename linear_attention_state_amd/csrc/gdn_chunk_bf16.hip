@@ -21,11 +21,21 @@
 // U' is split into bf16 hi + lo parts for the state update, and P and U' are both split
 // for P U' (hi*hi + hi*lo + lo*hi).  Everything else is a single bf16 rounding.
 //
-// Work decomposition: one workgroup per (sequence, value head).  Wave w owns value
-// columns [32w, 32w + 32) of the state, kept in MFMA accumulator registers as S^T tiles
-// (dk rows x 32 dv columns).  Chunk-local quantities (L, A, W, P) are shared through LDS.
-// The accumulator layout of one product is fed straight back as the B operand of the
-// next by permuting the contraction index consistently on both operands (see kperm()).
+// Work decomposition: one workgroup of DV/32 waves per (sequence, value head); two
+// workgroups share a CU (LDS <= 80 KiB, <= 256 registers per lane) so that one's
+// barriers and latencies hide behind the other's MFMA work.  Wave w owns value columns
+// [32w, 32w + 32) of the state, kept in MFMA accumulator registers as S^T tiles (dk rows
+// x 32 dv columns).  Per chunk:
+//   P0  stage K, Q (row-major) in LDS; gate cumsum; prefetch the next chunk's K, Q, g, beta
+//   P1  K K^T and Q K^T, lower 16x16 tiles on 16x16x32 MFMA; L to LDS, Q K^T kept in registers
+//   P2  A = (I + L)^{-1} on one wave: fp32 forward substitution of the four 16x16 diagonal
+//       blocks (a 16-lane group per block), 16x16x16 MFMA merges held in registers
+//   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
+//       K^T operands come from the row-major K tile through LDS transpose reads
+//   P4  P (bf16 hi/lo) to LDS, over the dead (A - I) tiles
+//   P5  U' = U0 + (-W) S^T ;  O = e^gamma q_scale Q S^T + P U' ;  S update
+// An accumulator feeds the next product directly as its B operand: the contraction index
+// is permuted the same way on both operands (see kperm()).
 #include "internal.h"
 
 namespace tr {
@@ -34,15 +44,19 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;                 // tokens per chunk
-constexpr int RS_T = CH + 8;           // row stride (elements) of token-contiguous tiles
+constexpr int RS_T = CH + 8;           // row stride (elements) of 64-column bf16 tiles
 constexpr int RS_L = CH + 4;           // row stride of the fp32 L tile
 
 __device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -53,33 +67,35 @@ __device__ __forceinline__ f32x16 zero16() {
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
     return z;
 }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// a + 4p supplies the address of row R_p, columns [c + 4a, c + 4a + 4) of a row-major
+// tile; lane 4a + b then receives column c + 4a + b at rows R_0..R_3.
+__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = lo[i]; r[4 + i] = hi[i]; }
+    return r;
+}
 
 // 32x32x16 MFMA layouts (lane l, half h = l / 32):
 //   A operand: row l % 32, k = 8h + i;  B operand: column l % 32, k = 8h + i;
 //   accumulator register j: row 8 (j / 4) + 4h + (j % 4), column l % 32.
 // When an accumulator (rows = contraction index) is reused as a B operand, k-step s of
 // 16 rows takes registers 8 (s % 2) .. 8 (s % 2) + 7 of row tile s / 2, which hold rows
-// 16 s + {4h .. 4h+3} and 16 s + 8 + {4h .. 4h+3}.  kperm() reads the partner operand's
-// row in that same order.
+// 16 s + {4h .. 4h+3} and 16 s + 8 + {4h .. 4h+3}.  kperm() reads a partner row in that
+// same order, and the transpose reads below fetch token columns in it.
 __device__ __forceinline__ int acc_row(int j, int h) { return 8 * (j >> 2) + 4 * h + (j & 3); }
 
 __device__ __forceinline__ bf16x8 kperm(const bf16* row, int s, int h) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * s + 4 * h);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * s + 8 + 4 * h);
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { r[i] = lo[i]; r[4 + i] = hi[i]; }
-    return r;
-}
-__device__ __forceinline__ bf16x8 kstd(const bf16* row, int s, int h) {
-    return *reinterpret_cast<const bf16x8*>(row + 16 * s + 8 * h);
-}
-// B operand for k-step s from an fp32 accumulator tile (registers 8 (s % 2) ..).
-__device__ __forceinline__ bf16x8 acc_to_b(const f32x16& t, int s) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (bf16)t[8 * (s & 1) + i];
-    return r;
+    return cat(*reinterpret_cast<const bf16x4*>(row + 16 * s + 4 * h),
+               *reinterpret_cast<const bf16x4*>(row + 16 * s + 8 + 4 * h));
 }
 __device__ __forceinline__ void acc_to_b_split(const f32x16& t, int s, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -90,28 +106,73 @@ __device__ __forceinline__ void acc_to_b_split(const f32x16& t, int s, bf16x8& h
         lo[i] = (bf16)(x - (float)xh);
     }
 }
+__device__ __forceinline__ bf16x8 acc_to_b(const f32x16& t, int s) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)t[8 * (s & 1) + i];
+    return r;
+}
+__device__ __forceinline__ bf16x4 to_bf4(const f32x4& x, float sign) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (bf16)(sign * x[i]);
+    return r;
+}
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() would also wait for every
+// outstanding global load, including the next chunk's prefetch issued just before it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    float y;
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
+    x += y;   // row_shr:1
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+    x += y;   // row_shr:2
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+    x += y;   // row_shr:4
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+    x += y;   // row_shr:8
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+    x += y;   // row_bcast:15 into rows 1 and 3
+    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+    x += y;   // row_bcast:31 into rows 2 and 3
+    return x;
+}
 
 template <int DK, int DV>
 struct Smem {
-    bf16 K[CH][DK + 8];         // token rows
-    bf16 Q[CH][DK + 8];
-    bf16 KT[DK][RS_T];          // key columns: K^T, token contiguous
-    bf16 VT[DV][RS_T];          // V^T
+    bf16 K[CH][DK + 16];        // key rows (padding keeps the transpose reads conflict-free)
+    bf16 Q[CH][DK + 8];         // query rows
     union {
-        float L[CH][RS_L];      // strictly lower L (fp32), live until the inverse is done
-        bf16 W[CH][DK + 8];     // W rows, live from the W product to the end of the chunk
+        float L[CH][RS_L];      // strictly lower L, fp32: P1 .. P2
+        bf16 Wn[CH][DK + 8];    // -W rows: P3 .. P5
     } lw;
-    bf16 Ab[CH][RS_T];          // blocks of A = (I + L)^{-1} as bf16 merge operands
-    bf16 Nb[CH][RS_T];          // (A - I) diag(beta)
-    bf16 Nbg[CH][RS_T];         // (A - I) diag(beta e^gamma)
-    bf16 Ph[CH][RS_T];          // P, bf16 high part
-    bf16 Pl[CH][RS_T];          // P, bf16 low part
-    float gam[CH];
-    float beta[CH];
+    union {
+        struct { bf16 Nb[CH][RS_T]; bf16 Nbg[CH][RS_T]; } n;   // (A-I) diag(beta), (A-I) diag(beta e^g): P2 .. P3
+        struct { bf16 Ph[CH][RS_T]; bf16 Pl[CH][RS_T]; } p;    // P hi / lo: P4 .. P5
+    } np;
+    bf16 Ad[4][16][24];         // diagonal 16x16 blocks of A (bf16 merge operands)
+    // per-token tables of the chunk (padded tokens: g = beta = 0)
+    float g2[CH];               // gamma_t * log2(e)
+    float bt[CH];               // beta_t
+    float bg[CH];               // beta_t e^{gamma_t}
+    float eg[CH];               // e^{gamma_t}
+    float dec[CH];              // e^{gamma_last - gamma_t}
 };
 
+// Four consecutive table entries starting at a multiple of 4.
+__device__ __forceinline__ f32x4 tab4(const float* t, int i) { return *reinterpret_cast<const f32x4*>(t + i); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int DK, int DV>
-__global__ void __launch_bounds__(DV * 2, 1)
+__global__ void __launch_bounds__(DV * 2, 2)
 gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -119,20 +180,29 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const float* state_in, float* state_out, bf16* __restrict__ o)
 {
     constexpr int NW = DV / 32;            // waves; wave w owns dv columns [32w, 32w+32)
-    constexpr int NT = NW * 64;            // threads
+    constexpr int NT = NW * 64;
     constexpr int KT_TILES = DK / 32;      // S^T row tiles per wave
-    constexpr int KSTEPS_D = DK / 16;      // k-steps over dk
+    constexpr int KSTEPS_D = DK / 16;      // 32x32x16 k-steps over dk
+    constexpr int TPR = DK / 8;            // threads per staged key/query row (16 B each)
+    constexpr int RPP = NT / TPR;          // rows per pass
+    constexpr int NPASS = CH / RPP;
+    constexpr int G_PER_WAVE = (10 + NW - 1) / NW;          // K K^T tiles per wave (P1)
+    constexpr int QK_PER_WAVE = (10 + NW - 2) / (NW - 1);   // Q K^T tiles per wave 1.. (P2)
+    constexpr float LOG2E = 1.4426950408889634f;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem<DK, DV>& sm = *reinterpret_cast<Smem<DK, DV>*>(smem_raw);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int h2 = lane >> 5;              // half of the wave (32x32 layouts)
-    const int l16 = lane & 15;
-    const int g4 = lane >> 4;              // quarter of the wave (16x16 layouts)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int lane = tid & 63;
+    int l32 = lane & 31;
+    int h2 = lane >> 5;
+    int l16 = lane & 15;
+    int g4 = lane >> 4;
+    // transpose-read addressing: row offset p and column offset within a 32-wide tile
+    int tr_p = (lane & 15) >> 2;
+    int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     const int b = blockIdx.x / Hv;
     const int hv = blockIdx.x % Hv;
@@ -140,319 +210,406 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int bos = cu ? cu[b] : b * uniform_len;
     const int len = cu ? cu[b + 1] - bos : uniform_len;
     const int n_chunks = (len + CH - 1) / CH;
-    const int col0 = 32 * wave;            // this wave's first dv column
+    const int col0 = 32 * wave;
+
+    // Buffer views of this (sequence, head): rows past the sequence end read as zero.
+    const uint32_t kq_stride = (uint32_t)Hqk * DK * 2;     // bytes between token rows
+    const uint32_t v_stride = (uint32_t)Hv * DV * 2;
+    const uint32_t gb_stride = (uint32_t)Hv * 4;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + ((size_t)bos * Hqk + hq) * DK, (uint32_t)len * kq_stride);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + ((size_t)bos * Hqk + hq) * DK, (uint32_t)len * kq_stride);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + ((size_t)bos * Hv + hv) * DV, (uint32_t)len * v_stride);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
 
     // ---- state: S^T tiles, tile r covers dk rows [32r, 32r+32), columns = own dv cols
     f32x16 St[KT_TILES];
-    {
-        const size_t base = (size_t)b * state_bstride + (size_t)hv * DV * DK;
+    const size_t sbase = (size_t)b * state_bstride + (size_t)hv * DV * DK + (size_t)(col0 + l32) * DK;
 #pragma unroll
-        for (int r = 0; r < KT_TILES; ++r) {
-            if (state_in) {
+    for (int r = 0; r < KT_TILES; ++r) {
+        if (state_in) {
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int dk0 = 32 * r + 8 * q4 + 4 * h2;
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(state_in + base + (size_t)(col0 + l32) * DK + dk0);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(state_in + sbase + 32 * r + 8 * q4 + 4 * h2);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) St[r][4 * q4 + i] = x[i];
-                }
-            } else {
-                St[r] = zero16();
+                for (int i = 0; i < 4; ++i) St[r][4 * q4 + i] = x[i];
             }
+        } else {
+            St[r] = zero16();
         }
     }
 
-    // Nb / Nbg: blocks above the diagonal are never written below; clear them once.
+    // (A - I) tiles above the diagonal inside each 32-row band are read as zeros and never
+    // written by the inverse; P4 rewrites them as zeros each chunk (the tiles alias P).
     for (int i = tid; i < CH * RS_T; i += NT) {
-        (&sm.Nb[0][0])[i] = (bf16)0.f;
-        (&sm.Nbg[0][0])[i] = (bf16)0.f;
+        (&sm.np.n.Nb[0][0])[i] = (bf16)0.f;
+        (&sm.np.n.Nbg[0][0])[i] = (bf16)0.f;
     }
 
+    // ---- loads (zero past the end of the sequence)
+    bf16x8 pk[NPASS], pq[NPASS];
+    float pg = 0.f, pb = 0.f;
+    int kq_row = tid / TPR;
+    int kq_col = (tid % TPR) * 8;
+    // K and the gates are prefetched one chunk ahead; Q is loaded at the start of its own
+    // chunk and staged at the end of P1 (register budget).
+    auto fetch_kq = [&](int c) {
+        const uint32_t voff = (uint32_t)kq_row * kq_stride + (uint32_t)kq_col * 2;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const uint32_t soff = (uint32_t)(c * CH + RPP * p) * kq_stride;
+            pk[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, voff, soff, 0));
+        }
+        if (wave == 0) {
+            const uint32_t soff = (uint32_t)(c * CH) * gb_stride;
+            pg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)lane * gb_stride, soff, 0));
+            pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * gb_stride, soff, 0));
+        }
+    };
+    if (n_chunks > 0) fetch_kq(0);
+
     for (int c = 0; c < n_chunks; ++c) {
+        // Recompute the lane-derived indices every chunk: left loop-invariant, the compiler
+        // hoists dozens of per-lane LDS addresses out of the loop and spills them.
+        asm volatile("" : "+v"(lane));
+        l32 = lane & 31; h2 = lane >> 5; l16 = lane & 15; g4 = lane >> 4;
+        tr_p = (lane & 15) >> 2; tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        kq_row = (64 * wave + lane) / TPR; kq_col = ((64 * wave + lane) % TPR) * 8;
         const int t0 = bos + c * CH;
         const int nval = min(CH, len - c * CH);
 
-        // ------------------------------------------------------------ load the chunk
+        // -------------------------------------------------------------- P0: stage
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+            *reinterpret_cast<bf16x8*>(&sm.K[kq_row + RPP * p][kq_col]) = pk[p];
+        if (wave == 0) {
+            const float g2 = wave_prefix_sum(pg) * LOG2E;
+            const float g2_last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), 63));
+            const float e = __builtin_amdgcn_exp2f(g2);
+            sm.g2[lane] = g2;
+            sm.bt[lane] = pb;
+            sm.bg[lane] = pb * e;
+            sm.eg[lane] = e;
+            sm.dec[lane] = __builtin_amdgcn_exp2f(g2_last - g2);
+        }
+        // This chunk's Q and V are issued after the tables: the gate values reloaded above
+        // must not queue behind them.
         {
-            constexpr int TPR_K = DK / 8;              // threads per key row (16 B each)
-            constexpr int RPP_K = NT / TPR_K;          // rows per pass
-            const int cc = (tid % TPR_K) * 8;
-            for (int row = tid / TPR_K; row < CH; row += RPP_K) {
-                bf16x8 kx, qx;
-                if (row < nval) {
-                    const size_t off = ((size_t)(t0 + row) * Hqk + hq) * DK + cc;
-                    kx = *reinterpret_cast<const bf16x8*>(k + off);
-                    qx = *reinterpret_cast<const bf16x8*>(q + off);
-                } else {
+            const uint32_t voff = (uint32_t)kq_row * kq_stride + (uint32_t)kq_col * 2;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) { kx[i] = (bf16)0.f; qx[i] = (bf16)0.f; }
-                }
-                *reinterpret_cast<bf16x8*>(&sm.K[row][cc]) = kx;
-                *reinterpret_cast<bf16x8*>(&sm.Q[row][cc]) = qx;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sm.KT[cc + i][row] = kx[i];
-            }
-            constexpr int TPR_V = DV / 8;
-            constexpr int RPP_V = NT / TPR_V;
-            const int cv = (tid % TPR_V) * 8;
-            for (int row = tid / TPR_V; row < CH; row += RPP_V) {
-                bf16x8 vx;
-                if (row < nval) {
-                    vx = *reinterpret_cast<const bf16x8*>(v + ((size_t)(t0 + row) * Hv + hv) * DV + cv);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) vx[i] = (bf16)0.f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) sm.VT[cv + i][row] = vx[i];
-            }
-            if (wave == 0) {
-                // log-space gate cumsum over the chunk (padded tokens: g = 0, beta = 0)
-                float gv = 0.f, bv = 0.f;
-                if (lane < nval) {
-                    gv = g[(size_t)(t0 + lane) * Hv + hv];
-                    bv = beta[(size_t)(t0 + lane) * Hv + hv];
-                }
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float up = __shfl_up(gv, off, 64);
-                    if (lane >= off) gv += up;
-                }
-                sm.gam[lane] = gv;
-                sm.beta[lane] = bv;
+            for (int p = 0; p < NPASS; ++p) {
+                const uint32_t soff = (uint32_t)(c * CH + RPP * p) * kq_stride;
+                pq[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, voff, soff, 0));
             }
         }
-        __syncthreads();
 
-        // ------------------------------------- K K^T -> L and Q K^T -> P (3 lower tiles each)
-        // tiles: 0..2 = G(0,0), G(1,0), G(1,1); 3..5 = the same for Q K^T
-        for (int tile = wave; tile < 6; tile += NW) {
-            const bool is_p = tile >= 3;
-            const int tt = is_p ? tile - 3 : tile;
-            const int rb = tt == 0 ? 0 : 1;
-            const int cb = tt == 2 ? 1 : 0;
-            const bf16 (*X)[DK + 8] = is_p ? sm.Q : sm.K;
-            f32x16 acc = zero16();
+        // V of this wave's columns in B-operand order (k-step s holds tokens
+        // 16s + 4h + {0..3} and 16s + 8 + 4h + {0..3}); consumed in P3.
+        bf16x8 vc[4];
+        {
+            const uint32_t voff = (uint32_t)(4 * h2) * v_stride + (uint32_t)(col0 + l32) * 2;
 #pragma unroll
-            for (int s = 0; s < KSTEPS_D; ++s)
-                acc = mma32(kstd(&X[32 * rb + l32][0], s, h2), kstd(&sm.K[32 * cb + l32][0], s, h2), acc);
-            const int ci = 32 * cb + l32;          // column index i (token)
-            const float gi = sm.gam[ci];
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int rt = 32 * rb + acc_row(j, h2);     // row index t (token)
-                const float dec = __expf(sm.gam[rt] - gi);
-                if (!is_p) {
-                    sm.lw.L[rt][ci] = (ci < rt) ? sm.beta[rt] * dec * acc[j] : 0.f;
-                } else {
-                    const float p = (ci <= rt) ? q_scale * dec * acc[j] : 0.f;
-                    const bf16 ph = (bf16)p;
-                    sm.Ph[rt][ci] = ph;
-                    sm.Pl[rt][ci] = (bf16)(p - (float)ph);
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t soff = (uint32_t)(c * CH + 16 * s + (i & 3) + ((i >> 2) << 3)) * v_stride;
+                    vc[s][i] = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(rv, voff, soff, 0));
                 }
+        }
+
+        if (c + 1 < n_chunks) fetch_kq(c + 1);
+        lds_barrier();
+
+        // ------------------------------------------------------------- P1: K K^T -> L
+#pragma unroll
+        for (int it = 0; it < G_PER_WAVE; ++it) {
+            const int tt = wave + NW * it;
+            if (tt < 10) {
+                const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                const int cb = tt - rb * (rb + 1) / 2;
+                const bf16* xrow = &sm.K[16 * rb + l16][0];
+                const bf16* krow = &sm.K[16 * cb + l16][0];
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s)
+                    acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
+                                   *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
+                const int ci = 16 * cb + l16;
+                const float gi = sm.g2[ci];
+                const int r0 = 16 * rb + 4 * g4;
+                const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sm.lw.L[r0 + j][ci] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+            *reinterpret_cast<bf16x8*>(&sm.Q[kq_row + RPP * p][kq_col]) = pq[p];
+        lds_barrier();
 
-        // ------------------------------------------------ A = (I + L)^{-1}, blocked by 16
-        // diagonal blocks: forward substitution in fp32, one block per wave (column per lane)
-        for (int blk = wave; blk < 4; blk += NW) {
-            const int j = l16;
-            const int base = 16 * blk;
-            float a[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float acc = (t == j) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < t; ++i) acc -= sm.lw.L[base + t][base + i] * a[i];
-                a[t] = acc;
-            }
-            if (lane < 16) {
-                const float bj = sm.beta[base + j];
-                const float bgj = bj * __expf(sm.gam[base + j]);
+        // -------------------- P2: A = (I + L)^{-1} on wave 0; Q K^T on the other waves
+        f32x4 tacc[QK_PER_WAVE];
+        if (wave == 0) {
+            // diagonal blocks: 16-lane group g4 solves block g4, lane l16 owns column l16
+            {
+                const int base = 16 * g4;
+                const int j = l16;
+                float a[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
-                    sm.Ab[base + t][base + j] = (bf16)a[t];
-                    const float n = (t > j) ? a[t] : 0.f;
-                    sm.Nb[base + t][base + j] = (bf16)(n * bj);
-                    sm.Nbg[base + t][base + j] = (bf16)(n * bgj);
+                    float acc = (t == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < t; ++i) acc -= sm.lw.L[base + t][base + i] * a[i];
+                    a[t] = acc;
+                }
+                const float bj = sm.bt[base + j];
+                const float bgj = sm.bg[base + j];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    sm.Ad[g4][t][j] = (bf16)a[t];
+                    const float nn = (t > j) ? a[t] : 0.f;
+                    sm.np.n.Nb[base + t][base + j] = (bf16)(nn * bj);
+                    sm.np.n.Nbg[base + t][base + j] = (bf16)(nn * bgj);
                 }
             }
-        }
-        __syncthreads();
-        // off-diagonal blocks by distance: A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj
-        for (int dist = 1; dist < 4; ++dist) {
-            const int n_blocks = 4 - dist;
-            for (int bi = wave; bi < n_blocks; bi += NW) {
-                const int i = bi + dist;
-                const int j = bi;
-                f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
-                for (int kb = j; kb < i; ++kb) {
-                    bf16x4 la, ab;
-                    const float* lrow = &sm.lw.L[16 * i + l16][16 * kb + 4 * g4];
+            // merges: A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj, 16x16x16 MFMA.  16x16x16 layouts:
+            // A operand lane (m = l % 16, q = l / 16) holds row m, k = 4q..4q+3; B operand and
+            // accumulator hold rows 4q..4q+3 of column l % 16, so a result feeds the next
+            // product's B operand as it stands.
+            auto opL = [&](int i, int kb) {          // A operand: L block (i, kb)
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.lw.L[16 * i + l16][16 * kb + 4 * g4]);
+                return to_bf4(x, 1.f);
+            };
+            auto opAd = [&](int i) {                 // A operand: diagonal block A_ii
+                return *reinterpret_cast<const bf16x4*>(&sm.Ad[i][l16][4 * g4]);
+            };
+            auto opBd = [&](int kb) {                // B operand: diagonal block A_kk
+                bf16x4 r;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        la[r] = (bf16)lrow[r];
-                        ab[r] = sm.Ab[16 * kb + 4 * g4 + r][16 * j + l16];
-                    }
-                    t4 = mma16(la, ab, t4);
-                }
-                bf16x4 da, tb;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    da[r] = sm.Ab[16 * i + l16][16 * i + 4 * g4 + r];
-                    tb[r] = (bf16)(-t4[r]);
-                }
-                f32x4 res = {0.f, 0.f, 0.f, 0.f};
-                res = mma16(da, tb, res);
+                for (int e = 0; e < 4; ++e) r[e] = sm.Ad[kb][4 * g4 + e][l16];
+                return r;
+            };
+            auto emit = [&](int i, int j, const f32x4& x) {
                 const int cj = 16 * j + l16;
-                const float bj = sm.beta[cj];
-                const float bgj = bj * __expf(sm.gam[cj]);
+                const float bj = sm.bt[cj];
+                const float bgj = sm.bg[cj];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rt = 16 * i + 4 * g4 + r;
-                    sm.Ab[rt][cj] = (bf16)res[r];
-                    sm.Nb[rt][cj] = (bf16)(res[r] * bj);
-                    sm.Nbg[rt][cj] = (bf16)(res[r] * bgj);
+                for (int e = 0; e < 4; ++e) {
+                    const int rt = 16 * i + 4 * g4 + e;
+                    sm.np.n.Nb[rt][cj] = (bf16)(x[e] * bj);
+                    sm.np.n.Nbg[rt][cj] = (bf16)(x[e] * bgj);
+                }
+            };
+            // distance 1
+            f32x4 a10 = mma16(opL(1, 0), opBd(0), zero4());
+            f32x4 a21 = mma16(opL(2, 1), opBd(1), zero4());
+            f32x4 a32 = mma16(opL(3, 2), opBd(2), zero4());
+            a10 = mma16(opAd(1), to_bf4(a10, -1.f), zero4());
+            a21 = mma16(opAd(2), to_bf4(a21, -1.f), zero4());
+            a32 = mma16(opAd(3), to_bf4(a32, -1.f), zero4());
+            emit(1, 0, a10); emit(2, 1, a21); emit(3, 2, a32);
+            // distance 2
+            const bf16x4 b10 = to_bf4(a10, 1.f), b21 = to_bf4(a21, 1.f);
+            f32x4 a20 = mma16(opL(2, 1), b10, mma16(opL(2, 0), opBd(0), zero4()));
+            f32x4 a31 = mma16(opL(3, 2), b21, mma16(opL(3, 1), opBd(1), zero4()));
+            a20 = mma16(opAd(2), to_bf4(a20, -1.f), zero4());
+            a31 = mma16(opAd(3), to_bf4(a31, -1.f), zero4());
+            emit(2, 0, a20); emit(3, 1, a31);
+            // distance 3
+            f32x4 a30 = mma16(opL(3, 0), opBd(0), zero4());
+            a30 = mma16(opL(3, 1), b10, a30);
+            a30 = mma16(opL(3, 2), to_bf4(a20, 1.f), a30);
+            a30 = mma16(opAd(3), to_bf4(a30, -1.f), zero4());
+            emit(3, 0, a30);
+        } else {
+            // Q K^T lower 16x16 tiles, kept in registers until P4
+#pragma unroll
+            for (int it = 0; it < QK_PER_WAVE; ++it) {
+                const int tt = (wave - 1) + (NW - 1) * it;
+                if (tt < 10) {
+                    const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                    const int cb = tt - rb * (rb + 1) / 2;
+                    const bf16* xrow = &sm.Q[16 * rb + l16][0];
+                    const bf16* krow = &sm.K[16 * cb + l16][0];
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < DK / 32; ++s)
+                        acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
+                                       *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
+                    tacc[it] = acc;
                 }
             }
-            __syncthreads();
         }
+        lds_barrier();
 
-        // ------------------------------------------- U0 (own dv columns) and W (dk tiles)
+        // --------------------------------------------------------- P3: U0 and -W
         f32x16 U[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             f32x16 acc = zero16();
-            const int ns = rt == 0 ? 2 : 4;          // A is lower triangular
-            for (int s = 0; s < ns; ++s)
-                acc = mma32(kstd(&sm.Nb[32 * rt + l32][0], s, h2), kstd(&sm.VT[col0 + l32][0], s, h2), acc);
+#pragma unroll
+            for (int s = 0; s < 2 * rt + 2; ++s)             // A = (I + L)^{-1} is lower triangular
+                acc = mma32(kperm(&sm.np.n.Nb[32 * rt + l32][0], s, h2), vc[s], acc);
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
-                const int t = 32 * rt + 8 * j4 + 4 * h2;
-                const bf16x4 vv = *reinterpret_cast<const bf16x4*>(&sm.VT[col0 + l32][t]);
+                const f32x4 bt = tab4(sm.bt, 32 * rt + 8 * j4 + 4 * h2);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[4 * j4 + r] += sm.beta[t + r] * (float)vv[r];
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * j4 + e;
+                    acc[j] += bt[e] * (float)vc[2 * rt + (j >> 3)][j & 7];
+                }
             }
             U[rt] = acc;
         }
         for (int ct = wave; ct < DK / 32; ct += NW) {
+            bf16x8 kb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kb[s] = cat(lds_tr4(&sm.K[16 * s + 4 * h2 + tr_p][32 * ct + tr_c]),
+                            lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * ct + tr_c]));
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 f32x16 acc = zero16();
-                const int ns = rt == 0 ? 2 : 4;
-                for (int s = 0; s < ns; ++s)
-                    acc = mma32(kstd(&sm.Nbg[32 * rt + l32][0], s, h2), kstd(&sm.KT[32 * ct + l32][0], s, h2), acc);
+#pragma unroll
+                for (int s = 0; s < 2 * rt + 2; ++s)
+                    acc = mma32(kperm(&sm.np.n.Nbg[32 * rt + l32][0], s, h2), kb[s], acc);
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
-                    const int t = 32 * rt + 8 * j4 + 4 * h2;
-                    const bf16x4 kk = *reinterpret_cast<const bf16x4*>(&sm.KT[32 * ct + l32][t]);
+                    const int t4 = 32 * rt + 8 * j4 + 4 * h2;
+                    const f32x4 bg = tab4(sm.bg, t4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float w = acc[4 * j4 + r] + sm.beta[t + r] * __expf(sm.gam[t + r]) * (float)kk[r];
-                        sm.lw.W[t + r][32 * ct + l32] = (bf16)w;
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 4 * j4 + e;
+                        const float w = acc[j] + bg[e] * (float)kb[2 * rt + (j >> 3)][j & 7];
+                        sm.lw.Wn[t4 + e][32 * ct + l32] = (bf16)(-w);
                     }
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ------------------------------------------------------ state-dependent part
-        bf16x8 Sb[KSTEPS_D];
+        // ------------------------------------------------------------ P4: P to LDS
+        if (o && wave > 0) {
 #pragma unroll
-        for (int s = 0; s < KSTEPS_D; ++s) Sb[s] = acc_to_b(St[s >> 1], s);
-
-        // U' = U0 - W S^T ;  Y = Q S^T
-        f32x16 Y[2];
+            for (int it = 0; it < QK_PER_WAVE; ++it) {
+                const int tt = (wave - 1) + (NW - 1) * it;
+                if (tt < 10) {
+                    const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                    const int cb = tt - rb * (rb + 1) / 2;
+                    const int ci = 16 * cb + l16;
+                    const float gi = sm.g2[ci];
+                    const int r0 = 16 * rb + 4 * g4;
+                    const f32x4 gt = tab4(sm.g2, r0);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            f32x16 x = zero16();
-#pragma unroll
-            for (int s = 0; s < KSTEPS_D; ++s) x = mma32(kperm(&sm.lw.W[32 * rt + l32][0], s, h2), Sb[s], x);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) U[rt][j] -= x[j];
-            if (o) {
-                f32x16 y = zero16();
-#pragma unroll
-                for (int s = 0; s < KSTEPS_D; ++s) y = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), Sb[s], y);
-                Y[rt] = y;
-            }
-        }
-
-        // O = diag(e^gamma) Y + P U'
-        if (o) {
-            bf16x8 uh[4], ul[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, uh[s], ul[s]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x16 acc = zero16();
-                const int ns = rt == 0 ? 2 : 4;
-#pragma unroll
-                for (int s = 0; s < ns; ++s) {
-                    const bf16x8 ph = kperm(&sm.Ph[32 * rt + l32][0], s, h2);
-                    const bf16x8 pl = kperm(&sm.Pl[32 * rt + l32][0], s, h2);
-                    acc = mma32(ph, uh[s], acc);
-                    acc = mma32(ph, ul[s], acc);
-                    acc = mma32(pl, uh[s], acc);
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int t = 32 * rt + acc_row(j, h2);
-                    if (t < nval) {
-                        const float val = q_scale * __expf(sm.gam[t]) * Y[rt][j] + acc[j];
-                        o[((size_t)(t0 + t) * Hv + hv) * DV + col0 + l32] = (bf16)val;
+                    for (int j = 0; j < 4; ++j) {
+                        const float p = (ci <= r0 + j) ? q_scale * __builtin_amdgcn_exp2f(gt[j] - gi) * tacc[it][j] : 0.f;
+                        const bf16 ph = (bf16)p;
+                        sm.np.p.Ph[r0 + j][ci] = ph;
+                        sm.np.p.Pl[r0 + j][ci] = (bf16)(p - (float)ph);
                     }
                 }
             }
         }
+        if (wave == 0) {
+            // the zero blocks above the diagonal inside each 32-row band (also zero for A - I)
+#pragma unroll
+            for (int band = 0; band < 2; ++band)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rt = 32 * band + 4 * g4 + j;
+                    const int ci = 32 * band + 16 + l16;
+                    sm.np.p.Ph[rt][ci] = (bf16)0.f;
+                    sm.np.p.Pl[rt][ci] = (bf16)0.f;
+                }
+        }
+        lds_barrier();
 
-        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K
+        // ------------------------------------------------ P5: state-dependent part
+        // Register budget: the state (64), U' (32) and one 32-row output tile (16) are the
+        // only large live sets; S operands are converted per k-step.
         {
-            const float gl = sm.gam[CH - 1];
+            // U' = U0 + (-W) S^T
+#pragma unroll
+            for (int s = 0; s < KSTEPS_D; ++s) {
+                const bf16x8 sb = acc_to_b(St[s >> 1], s);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
+            }
+
+            if (o) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    f32x16 acc = zero16();
+#pragma unroll
+                    for (int s = 0; s < KSTEPS_D; ++s)
+                        acc = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), acc_to_b(St[s >> 1], s), acc);
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const f32x4 e = tab4(sm.eg, 32 * rt + 8 * j4 + 4 * h2);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[4 * j4 + i] *= q_scale * e[i];
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2 * rt + 2; ++s) {
+                        bf16x8 uh, ul;
+                        acc_to_b_split(U[s >> 1], s, uh, ul);
+                        const bf16x8 ph = kperm(&sm.np.p.Ph[32 * rt + l32][0], s, h2);
+                        const bf16x8 pl = kperm(&sm.np.p.Pl[32 * rt + l32][0], s, h2);
+                        acc = mma32(ph, uh, acc);
+                        acc = mma32(ph, ul, acc);
+                        acc = mma32(pl, uh, acc);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int t = 32 * rt + acc_row(j, h2);
+                        if (t < nval) o[((size_t)(t0 + t) * Hv + hv) * DV + col0 + l32] = (bf16)acc[j];
+                    }
+                }
+            }
+
+            // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const f32x4 d = tab4(sm.dec, 32 * rt + 8 * j4 + 4 * h2);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) U[rt][4 * j4 + i] *= d[i];
+                }
             bf16x8 dh[4], dl[4];
 #pragma unroll
+            for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, dh[s], dl[s]);
+            const float decay = sm.eg[CH - 1];
+#pragma unroll
+            for (int r = 0; r < KT_TILES; ++r)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) St[r][j] *= decay;
+            // k-step outer, tile inner: consecutive MFMAs hit independent accumulators
+#pragma unroll
             for (int s = 0; s < 4; ++s) {
-                f32x16 tmp;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int j = 8 * (s & 1) + i;
-                    const int t = 32 * (s >> 1) + acc_row(j, h2);
-                    tmp[j] = U[s >> 1][j] * __expf(gl - sm.gam[t]);
+                for (int r = 0; r < KT_TILES; ++r) {
+                    const bf16x8 a = cat(lds_tr4(&sm.K[16 * s + 4 * h2 + tr_p][32 * r + tr_c]),
+                                         lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * r + tr_c]));
+                    St[r] = mma32(a, dh[s], St[r]);
+                    St[r] = mma32(a, dl[s], St[r]);
                 }
-                acc_to_b_split(tmp, s, dh[s], dl[s]);
-            }
-            const float decay = __expf(gl);
-#pragma unroll
-            for (int r = 0; r < KT_TILES; ++r) {
-                f32x16 acc;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) acc[j] = St[r][j] * decay;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 a = kperm(&sm.KT[32 * r + l32][0], s, h2);
-                    acc = mma32(a, dh[s], acc);
-                    acc = mma32(a, dl[s], acc);
-                }
-                St[r] = acc;
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // ---- write the final state
-    {
-        const size_t base = (size_t)b * state_bstride + (size_t)hv * DV * DK;
 #pragma unroll
-        for (int r = 0; r < KT_TILES; ++r) {
+    for (int r = 0; r < KT_TILES; ++r) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int dk0 = 32 * r + 8 * q4 + 4 * h2;
-                f32x4 x;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 x;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = St[r][4 * q4 + i];
-                *reinterpret_cast<f32x4*>(state_out + base + (size_t)(col0 + l32) * DK + dk0) = x;
-            }
+            for (int i = 0; i < 4; ++i) x[i] = St[r][4 * q4 + i];
+            *reinterpret_cast<f32x4*>(state_out + sbase + 32 * r + 8 * q4 + 4 * h2) = x;
         }
     }
 }
