@@ -148,7 +148,7 @@ struct Smem {
     bf16 K[CH][DK + 16];        // key rows (padding keeps the transpose reads conflict-free)
     bf16 Q[CH][DK + 8];         // query rows
     union {
-        float L[CH][RS_L];      // strictly lower L, fp32: P1 .. P2
+        float LT[CH][RS_L];     // L transposed (LT[i][t] = L_ti, i < t), fp32: P1 .. P2
         bf16 Wn[CH][DK + 8];    // -W rows: P3 .. P5
     } lw;
     union {
@@ -161,6 +161,7 @@ struct Smem {
     float bt[CH];               // beta_t
     float bg[CH];               // beta_t e^{gamma_t}
     float eg[CH];               // e^{gamma_t}
+    float qeg[CH];              // q_scale e^{gamma_t}
     float dec[CH];              // e^{gamma_last - gamma_t}
 };
 
@@ -221,6 +222,8 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + ((size_t)bos * Hv + hv) * DV, (uint32_t)len * v_stride);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
+    // outputs: stores past the sequence end fall outside the resource and are dropped
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o ? o + ((size_t)bos * Hv + hv) * DV : nullptr, o ? (uint32_t)len * v_stride : 0u);
 
     // ---- state: S^T tiles, tile r covers dk rows [32r, 32r+32), columns = own dv cols
     f32x16 St[KT_TILES];
@@ -290,6 +293,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             sm.bt[lane] = pb;
             sm.bg[lane] = pb * e;
             sm.eg[lane] = e;
+            sm.qeg[lane] = q_scale * e;
             sm.dec[lane] = __builtin_amdgcn_exp2f(g2_last - g2);
         }
         // This chunk's Q and V are issued after the tables: the gate values reloaded above
@@ -338,9 +342,11 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 const float gi = sm.g2[ci];
                 const int r0 = 16 * rb + 4 * g4;
                 const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
+                f32x4 lv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    sm.lw.L[r0 + j][ci] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
+                    lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
+                *reinterpret_cast<f32x4*>(&sm.lw.LT[ci][r0]) = lv;
             }
         }
 #pragma unroll
@@ -351,35 +357,52 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         // -------------------- P2: A = (I + L)^{-1} on wave 0; Q K^T on the other waves
         f32x4 tacc[QK_PER_WAVE];
         if (wave == 0) {
-            // diagonal blocks: 16-lane group g4 solves block g4, lane l16 owns column l16
+            // Diagonal blocks D_b = (I + L_bb)^{-1}: the 16-lane group g4 takes block g4 and lane
+            // j solves (I + L_bb^T) y = e_j by back substitution, so y is row j of D_b and the
+            // block leaves the lane as whole rows.
             {
                 const int base = 16 * g4;
                 const int j = l16;
-                float a[16];
+                float y[16];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    float acc = (t == j) ? 1.f : 0.f;
+                for (int i = 15; i >= 0; --i) {
+                    float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                    for (int i = 0; i < t; ++i) acc -= sm.lw.L[base + t][base + i] * a[i];
-                    a[t] = acc;
+                    for (int kk = i + 1; kk < 16; ++kk) acc -= sm.lw.LT[base + i][base + kk] * y[kk];
+                    y[i] = acc;
                 }
-                const float bj = sm.bt[base + j];
-                const float bgj = sm.bg[base + j];
+                bf16x8 ad0, ad1, nb0, nb1, ng0, ng1;
 #pragma unroll
-                for (int t = 0; t < 16; ++t) {
-                    sm.Ad[g4][t][j] = (bf16)a[t];
-                    const float nn = (t > j) ? a[t] : 0.f;
-                    sm.np.n.Nb[base + t][base + j] = (bf16)(nn * bj);
-                    sm.np.n.Nbg[base + t][base + j] = (bf16)(nn * bgj);
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 bt = tab4(sm.bt, base + 4 * i4), bg = tab4(sm.bg, base + 4 * i4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        const float nn = (i < j) ? y[i] : 0.f;
+                        bf16x8& ad = i < 8 ? ad0 : ad1;
+                        bf16x8& nb = i < 8 ? nb0 : nb1;
+                        bf16x8& ng = i < 8 ? ng0 : ng1;
+                        ad[i & 7] = (bf16)y[i];
+                        nb[i & 7] = (bf16)(nn * bt[e]);
+                        ng[i & 7] = (bf16)(nn * bg[e]);
+                    }
                 }
+                *reinterpret_cast<bf16x8*>(&sm.Ad[g4][j][0]) = ad0;
+                *reinterpret_cast<bf16x8*>(&sm.Ad[g4][j][8]) = ad1;
+                *reinterpret_cast<bf16x8*>(&sm.np.n.Nb[base + j][base]) = nb0;
+                *reinterpret_cast<bf16x8*>(&sm.np.n.Nb[base + j][base + 8]) = nb1;
+                *reinterpret_cast<bf16x8*>(&sm.np.n.Nbg[base + j][base]) = ng0;
+                *reinterpret_cast<bf16x8*>(&sm.np.n.Nbg[base + j][base + 8]) = ng1;
             }
             // merges: A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj, 16x16x16 MFMA.  16x16x16 layouts:
             // A operand lane (m = l % 16, q = l / 16) holds row m, k = 4q..4q+3; B operand and
             // accumulator hold rows 4q..4q+3 of column l % 16, so a result feeds the next
             // product's B operand as it stands.
-            auto opL = [&](int i, int kb) {          // A operand: L block (i, kb)
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.lw.L[16 * i + l16][16 * kb + 4 * g4]);
-                return to_bf4(x, 1.f);
+            auto opL = [&](int i, int kb) {          // A operand: L block (i, kb), from L^T
+                bf16x4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = (bf16)sm.lw.LT[16 * kb + 4 * g4 + e][16 * i + l16];
+                return r;
             };
             auto opAd = [&](int i) {                 // A operand: diagonal block A_ii
                 return *reinterpret_cast<const bf16x4*>(&sm.Ad[i][l16][4 * g4]);
@@ -390,38 +413,40 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 for (int e = 0; e < 4; ++e) r[e] = sm.Ad[kb][4 * g4 + e][l16];
                 return r;
             };
-            auto emit = [&](int i, int j, const f32x4& x) {
-                const int cj = 16 * j + l16;
-                const float bj = sm.bt[cj];
-                const float bgj = sm.bg[cj];
+            // Block (i, j) of A - I is -(A_ii T); its transpose -(T^T A_ii^T) comes out of the MFMA
+            // in row order (lane (n, q) holds row n, columns 4q..4q+3), so it is written as
+            // 8-byte row segments.  T enters as the A operand in its accumulator layout (which
+            // reads as T^T), A_ii as the B operand in row layout (which reads as A_ii^T).
+            auto emit = [&](int i, int j, const bf16x4& tneg) {
+                const f32x4 rows = mma16(tneg, opAd(i), zero4());
+                const int c0 = 16 * j + 4 * g4;
+                const f32x4 bt = tab4(sm.bt, c0), bg = tab4(sm.bg, c0);
+                bf16x4 nb, ng;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int rt = 16 * i + 4 * g4 + e;
-                    sm.np.n.Nb[rt][cj] = (bf16)(x[e] * bj);
-                    sm.np.n.Nbg[rt][cj] = (bf16)(x[e] * bgj);
+                    nb[e] = (bf16)(rows[e] * bt[e]);
+                    ng[e] = (bf16)(rows[e] * bg[e]);
                 }
+                *reinterpret_cast<bf16x4*>(&sm.np.n.Nb[16 * i + l16][c0]) = nb;
+                *reinterpret_cast<bf16x4*>(&sm.np.n.Nbg[16 * i + l16][c0]) = ng;
             };
             // distance 1
-            f32x4 a10 = mma16(opL(1, 0), opBd(0), zero4());
-            f32x4 a21 = mma16(opL(2, 1), opBd(1), zero4());
-            f32x4 a32 = mma16(opL(3, 2), opBd(2), zero4());
-            a10 = mma16(opAd(1), to_bf4(a10, -1.f), zero4());
-            a21 = mma16(opAd(2), to_bf4(a21, -1.f), zero4());
-            a32 = mma16(opAd(3), to_bf4(a32, -1.f), zero4());
-            emit(1, 0, a10); emit(2, 1, a21); emit(3, 2, a32);
+            const bf16x4 t10 = to_bf4(mma16(opL(1, 0), opBd(0), zero4()), -1.f);
+            const bf16x4 t21 = to_bf4(mma16(opL(2, 1), opBd(1), zero4()), -1.f);
+            const bf16x4 t32 = to_bf4(mma16(opL(3, 2), opBd(2), zero4()), -1.f);
+            const bf16x4 b10 = to_bf4(mma16(opAd(1), t10, zero4()), 1.f);
+            const bf16x4 b21 = to_bf4(mma16(opAd(2), t21, zero4()), 1.f);
+            emit(1, 0, t10); emit(2, 1, t21); emit(3, 2, t32);
             // distance 2
-            const bf16x4 b10 = to_bf4(a10, 1.f), b21 = to_bf4(a21, 1.f);
-            f32x4 a20 = mma16(opL(2, 1), b10, mma16(opL(2, 0), opBd(0), zero4()));
-            f32x4 a31 = mma16(opL(3, 2), b21, mma16(opL(3, 1), opBd(1), zero4()));
-            a20 = mma16(opAd(2), to_bf4(a20, -1.f), zero4());
-            a31 = mma16(opAd(3), to_bf4(a31, -1.f), zero4());
-            emit(2, 0, a20); emit(3, 1, a31);
+            const bf16x4 t20 = to_bf4(mma16(opL(2, 1), b10, mma16(opL(2, 0), opBd(0), zero4())), -1.f);
+            const bf16x4 t31 = to_bf4(mma16(opL(3, 2), b21, mma16(opL(3, 1), opBd(1), zero4())), -1.f);
+            const bf16x4 b20 = to_bf4(mma16(opAd(2), t20, zero4()), 1.f);
+            emit(2, 0, t20); emit(3, 1, t31);
             // distance 3
             f32x4 a30 = mma16(opL(3, 0), opBd(0), zero4());
             a30 = mma16(opL(3, 1), b10, a30);
-            a30 = mma16(opL(3, 2), to_bf4(a20, 1.f), a30);
-            a30 = mma16(opAd(3), to_bf4(a30, -1.f), zero4());
-            emit(3, 0, a30);
+            a30 = mma16(opL(3, 2), b20, a30);
+            emit(3, 0, to_bf4(a30, -1.f));
         } else {
             // Q K^T lower 16x16 tiles, kept in registers until P4
 #pragma unroll
@@ -526,30 +551,34 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         lds_barrier();
 
         // ------------------------------------------------ P5: state-dependent part
-        // Register budget: the state (64), U' (32) and one 32-row output tile (16) are the
-        // only large live sets; S operands are converted per k-step.
+        // Register budget: the state (64), U' (32) and the two 32-row output tiles (32) are
+        // the large live sets; state operands are converted once per k-step.
         {
-            // U' = U0 + (-W) S^T
-#pragma unroll
-            for (int s = 0; s < KSTEPS_D; ++s) {
-                const bf16x8 sb = acc_to_b(St[s >> 1], s);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
-            }
-
+            // U' = U0 + (-W) S^T and, with outputs, Y = Q S^T: one conversion of each state
+            // operand feeds up to four independent accumulators.
+            f32x16 Y[2];
             if (o) {
+                Y[0] = zero16();
+                Y[1] = zero16();
+#pragma unroll
+                for (int s = 0; s < KSTEPS_D; ++s) {
+                    const bf16x8 sb = acc_to_b(St[s >> 1], s);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) {
+                        U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
+                        Y[rt] = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), sb, Y[rt]);
+                    }
+                }
+                // O = diag(q_scale e^gamma) Y + P U'
+                const uint32_t ooff = (uint32_t)(4 * h2) * v_stride + (uint32_t)(col0 + l32) * 2;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    f32x16 acc = zero16();
-#pragma unroll
-                    for (int s = 0; s < KSTEPS_D; ++s)
-                        acc = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), acc_to_b(St[s >> 1], s), acc);
+                    f32x16 acc = Y[rt];
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
-                        const f32x4 e = tab4(sm.eg, 32 * rt + 8 * j4 + 4 * h2);
+                        const f32x4 e = tab4(sm.qeg, 32 * rt + 8 * j4 + 4 * h2);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[4 * j4 + i] *= q_scale * e[i];
+                        for (int i = 0; i < 4; ++i) acc[4 * j4 + i] *= e[i];
                     }
 #pragma unroll
                     for (int s = 0; s < 2 * rt + 2; ++s) {
@@ -563,9 +592,17 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     }
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int t = 32 * rt + acc_row(j, h2);
-                        if (t < nval) o[((size_t)(t0 + t) * Hv + hv) * DV + col0 + l32] = (bf16)acc[j];
+                        const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)acc[j]), ro, ooff, soff, 0);
                     }
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KSTEPS_D; ++s) {
+                    const bf16x8 sb = acc_to_b(St[s >> 1], s);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
                 }
             }
 
