@@ -10,6 +10,8 @@
 // this is the plainest Gated DeltaNet layer body with the stated widths.
 #include "internal.h"
 
+#include <cstddef>
+
 namespace tr {
 namespace {
 
@@ -59,9 +61,21 @@ rmsnorm_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, PtrTable gain, 
 }
 
 // --------------------------------------------------------------------------- GEMM
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;            // bf16 elements per staged row
-constexpr int STAGE_STRIDE = BN + 4;          // fp32 elements per epilogue row
+// 256x256 output tile per workgroup of 8 waves (2 x 4 waves of 128x64, 32x32x16 bf16 MFMA).
+// The K loop streams 64-wide slices through a 2-slot LDS ring (64 KB per slot) with direct
+// global-to-LDS loads, issued one slice ahead.  Each 128-byte LDS row holds its eight 16-byte
+// chunks in a row-dependent order so that the operand reads hit distinct banks.
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int WAVES_N = 4, TM = 4, TN = 2;            // wave grid 2 x 4, wave tile 128 x 64
+constexpr int NTHREADS = 512;
+constexpr int ROW_BYTES = BK * 2;                    // 128
+constexpr int SLOT_BYTES = (BM + BN) * ROW_BYTES;    // A rows then B rows: 64 KB
+constexpr int SMEM_BYTES = 2 * SLOT_BYTES;           // 128 KB
+constexpr int LOADS_PER_WAVE = SLOT_BYTES / 1024 / (NTHREADS / 64);   // 1 KB per load instruction
+constexpr int GROUP_M = 8;                           // row tiles per band of the tile order
+constexpr int EPI_ROWS = 64;                         // the epilogue stages a quarter tile at a time
+constexpr int STAGE_STRIDE = BN + 4;                 // fp32 elements per staged row
+static_assert(EPI_ROWS * STAGE_STRIDE * 4 <= SMEM_BYTES, "epilogue staging must fit in the ring");
 
 enum { EPI_LAYER_IN = 0, EPI_RESIDUAL = 1 };
 
@@ -79,14 +93,25 @@ struct GemmParams {
     const bf16* x_in; bf16* x_out;
 };
 
+// Entry g of the pointer table at byte offset table_off of the kernel's argument block, read
+// straight from the kernel-argument segment (GemmParams is the kernel's only argument, at
+// offset 0).  Indexing the by-value argument with a variable would copy the whole block to
+// scratch memory.
+__device__ __forceinline__ const bf16* table_entry(size_t table_off, int g) {
+    typedef const __attribute__((address_space(4))) unsigned char kchar;
+    typedef const bf16* const __attribute__((address_space(4))) kptr;
+    kchar* ka = (kchar*)__builtin_amdgcn_kernarg_segment_ptr();
+    return *reinterpret_cast<kptr*>(ka + table_off + sizeof(void*) * (size_t)g);
+}
+
 __device__ __forceinline__ const bf16* row_src(const GemmParams& p, int g, int n) {
-    if (n < p.n0) return (const bf16*)p.b0.p[g] + (size_t)n * p.K;
+    if (n < p.n0) return table_entry(offsetof(GemmParams, b0), g) + (size_t)n * p.K;
     n -= p.n0;
-    if (n < p.n1) return (const bf16*)p.b1.p[g] + (size_t)n * p.K;
+    if (n < p.n1) return table_entry(offsetof(GemmParams, b1), g) + (size_t)n * p.K;
     n -= p.n1;
-    if (n < p.n2) return (const bf16*)p.b2.p[g] + (size_t)n * p.K;
+    if (n < p.n2) return table_entry(offsetof(GemmParams, b2), g) + (size_t)n * p.K;
     n -= p.n2;
-    if (n < p.n3) return (const bf16*)p.b3.p[g] + (size_t)n * p.K;
+    if (n < p.n3) return table_entry(offsetof(GemmParams, b3), g) + (size_t)n * p.K;
     return nullptr;
 }
 
@@ -96,166 +121,193 @@ __device__ __forceinline__ float sigmoid_f(float z) {
     return z >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
 }
 
+// Physical position of logical 16-byte chunk c in slot row r is c ^ chunk_swz(r).
+__device__ __forceinline__ int chunk_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int EPI>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(NTHREADS, 1)
 gemm_tn_kernel(const GemmParams p)
 {
-    __shared__ __align__(16) bf16 smem[2 * 2 * BM * LDS_STRIDE];   // [buf][A|B][row][k]
-    bf16 (*sA)[BM][LDS_STRIDE] = reinterpret_cast<bf16 (*)[BM][LDS_STRIDE]>(smem);
-    bf16 (*sB)[BN][LDS_STRIDE] = reinterpret_cast<bf16 (*)[BN][LDS_STRIDE]>(smem + 2 * BM * LDS_STRIDE);
+    extern __shared__ __align__(16) unsigned char smem[];
 
-    // XCD-aware tile order: consecutive logical tiles (same weight tile, successive row
-    // tiles) land on the same XCD, whose L2 then serves the shared weight rows.
-    const int n_tiles = p.G * p.n_mt * p.n_nt;
+    // Tile order: blocks of consecutive logical tiles go to one XCD (blockIdx % 8 picks the
+    // XCD), and inside a group the tiles run in bands of GROUP_M row tiles, so the tiles that
+    // an XCD holds at once share a few A row tiles and weight tiles in its L2.
+    const int per_group = p.n_mt * p.n_nt;
+    const int n_tiles = p.G * per_group;
     const int per_xcd = (int)((gridDim.x + 7) / 8);
     const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (logical >= n_tiles) return;
-    const int mt = logical % p.n_mt;
-    const int nt = (logical / p.n_mt) % p.n_nt;
-    const int g = logical / (p.n_mt * p.n_nt);
+    const int g = logical / per_group;
+    const int t = logical % per_group;
+    const int band = GROUP_M * p.n_nt;
+    const int first_m = (t / band) * GROUP_M;
+    const int rows_in_band = min(p.n_mt - first_m, GROUP_M);
+    const int mt = first_m + (t % band) % rows_in_band;
+    const int nt = (t % band) / rows_in_band;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h2 = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, h2 = lane >> 5;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    // loader: thread covers 16 B of rows r0 + 32 i, i = 0..3, column chunk kc
-    const int lr = tid >> 3;
-    const int kc = (tid & 7) * 8;
-    const bf16* a_src[4];
-    const bf16* b_src[4];
+    // Loader: load instruction i of a slot fills slot rows [8i, 8i + 8) (rows 0..255 are A,
+    // 256..511 are B); lane l writes bytes [16l, 16l + 16) of its 1 KB, i.e. row l / 8, chunk
+    // position l % 8.  Rows past M (or past the weight blocks) repeat a valid row: their
+    // results are never stored.
+    const bf16* src[LOADS_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = mt * BM + lr + 32 * i;
-        a_src[i] = (m < p.M) ? p.A + ((size_t)g * p.M + m) * p.K : nullptr;
-        b_src[i] = row_src(p, g, nt * BN + lr + 32 * i);
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+        const int r = (wave * LOADS_PER_WAVE + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ chunk_swz(r);
+        if (r < BM) {
+            const int m = min(mt * BM + r, p.M - 1);
+            src[j] = p.A + ((size_t)g * p.M + m) * p.K + 8 * c;
+        } else {
+            const bf16* br = row_src(p, g, nt * BN + r - BM);
+            src[j] = (br ? br : row_src(p, g, 0)) + 8 * c;
+        }
     }
-    bf16x8 ra[4], rb[4];
-    auto gload = [&](int k0) {
+    auto issue = [&](int kt) {
+        unsigned char* slot = smem + (kt & 1) * SLOT_BYTES + wave * LOADS_PER_WAVE * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (a_src[i]) ra[i] = *reinterpret_cast<const bf16x8*>(a_src[i] + k0 + kc);
-            else { for (int e = 0; e < 8; ++e) ra[i][e] = (bf16)0.f; }
-            if (b_src[i]) rb[i] = *reinterpret_cast<const bf16x8*>(b_src[i] + k0 + kc);
-            else { for (int e = 0; e < 8; ++e) rb[i][e] = (bf16)0.f; }
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<bf16x8*>(&sA[buf][lr + 32 * i][kc]) = ra[i];
-            *reinterpret_cast<bf16x8*>(&sB[buf][lr + 32 * i][kc]) = rb[i];
-        }
+        for (int j = 0; j < LOADS_PER_WAVE; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_void*)(slot + 1024 * j), 16, 0, 0);
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int KT = p.K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    const int KT = __builtin_amdgcn_readfirstlane(p.K / BK);
+    issue(0);
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload((kt + 1) * BK);
+        // slice kt is in LDS once this wave's loads are done and every wave has passed here;
+        // passing also means every wave is done reading the slot that slice kt + 1 overwrites
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (kt + 1 < KT) issue(kt + 1);
+        const unsigned char* slot = smem + (kt & 1) * SLOT_BYTES;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 af[2], bfr[2];
+            bf16x8 af[TM], bfr[TN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][64 * wm + 32 * i + l32][16 * kk + 8 * h2]);
-                bfr[i] = *reinterpret_cast<const bf16x8*>(&sB[cur][64 * wn + 32 * i + l32][16 * kk + 8 * h2]);
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * TM * 32 + 32 * i + l32;
+                af[i] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((2 * kk + h2) ^ chunk_swz(r)));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < TN; ++j) {
+                const int r = BM + wn * TN * 32 + 32 * j + l32;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((2 * kk + h2) ^ chunk_swz(r)));
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mma32(af[i], bfr[j], acc[i][j]);
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mma32(af[i], bfr[j], acc[i][j]);
         }
-        if (kt + 1 < KT) sstore(cur ^ 1);
-        __syncthreads();
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- epilogue: stage the fp32 tile in LDS, then rows are processed by thread pairs
+    // ---- epilogue, one 64-row quarter at a time: the waves holding that quarter stage their
+    // fp32 values in LDS, then eight threads take each row (32 columns each); four threads
+    // cover one 128-column segment (one head).
     float (*stage)[STAGE_STRIDE] = reinterpret_cast<float (*)[STAGE_STRIDE]>(smem);
+    const int er = tid >> 3;             // row within the quarter
+    const int eq = tid & 7;              // columns [32 eq, 32 eq + 32)
+    const float* srow = &stage[er][32 * eq];
+    const int seg = 2 * nt + (eq >> 2);  // 128-column segment of the output
+    // fully unrolled: the accumulator tiles must be indexed with constants to stay in registers
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int qr = 0; qr < BM / EPI_ROWS; ++qr) {
+        if (wm == (qr >> 1)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h2 + (e & 3);
-                stage[r][64 * wn + 32 * j + l32] = acc[i][j][e];
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = 32 * ii + 8 * (e >> 2) + 4 * h2 + (e & 3);
+                        stage[r][wn * TN * 32 + 32 * j + l32] = acc[2 * (qr & 1) + ii][j][e];
+                    }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+        const int m = mt * BM + EPI_ROWS * qr + er;
+        const bool valid = m < p.M;
+        const size_t grow = (size_t)g * p.M + m;      // global token row
+        if (EPI == EPI_RESIDUAL) {
+            const int n0 = nt * BN + 32 * eq;
+            if (valid && n0 < p.N) {
+                const bf16* xi = p.x_in + grow * p.N + n0;
+                bf16* xo = p.x_out + grow * p.N + n0;
+#pragma unroll
+                for (int c = 0; c < 32; c += 8) {
+                    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xi + c);
+                    bf16x8 ov;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)((float)xv[e] + srow[c + e]);
+                    *reinterpret_cast<bf16x8*>(xo + c) = ov;
+                }
             }
-    __syncthreads();
-
-    const int row = tid >> 1;            // tile row
-    const int half = tid & 1;            // columns [64 half, 64 half + 64)
-    const int m = mt * BM + row;
-    const bool valid = m < p.M;
-    const size_t grow = (size_t)g * p.M + m;      // global token row
-    const float* srow = &stage[row][64 * half];
-
-    if (EPI == EPI_RESIDUAL) {
-        if (!valid) return;
-        const int n0 = nt * BN + 64 * half;
-        const bf16* xi = p.x_in + grow * p.N + n0;
-        bf16* xo = p.x_out + grow * p.N + n0;
+        } else {
+            // EPI_LAYER_IN: segments are the q heads, the k heads, the v heads, then one
+            // segment of gate logits ([0, Hv) z_a, [Hv, 2 Hv) z_b)
+            float ss = 0.f;
 #pragma unroll
-        for (int c = 0; c < 64; c += 8) {
-            const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xi + c);
-            bf16x8 ov;
+            for (int c = 0; c < 32; ++c) ss = fmaf(srow[c], srow[c], ss);
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
+            if (valid && seg < nk) {
+                const bool is_q = seg < nq;
+                const float scale = (is_q ? p.q_scale : 1.f) / sqrtf(ss + 1e-6f);
+                const int head = is_q ? seg : seg - nq;
+                bf16* dst = (is_q ? p.q : p.k) + (grow * p.Hqk + head) * 128 + 32 * (eq & 3);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] = (bf16)((float)xv[e] + srow[c + e]);
-            *reinterpret_cast<bf16x8*>(xo + c) = ov;
+                for (int c = 0; c < 32; c += 8) {
+                    bf16x8 ov;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)(srow[c + e] * scale);
+                    *reinterpret_cast<bf16x8*>(dst + c) = ov;
+                }
+            } else if (valid && seg < nv) {
+                bf16* dst = p.v + (grow * p.Hv + (seg - nk)) * 128 + 32 * (eq & 3);
+#pragma unroll
+                for (int c = 0; c < 32; c += 8) {
+                    bf16x8 ov;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)srow[c + e];
+                    *reinterpret_cast<bf16x8*>(dst + c) = ov;
+                }
+            } else if (valid && seg == nv) {
+                for (int c = 0; c < 32; ++c) {
+                    const int cg = 32 * (eq & 3) + c;
+                    if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(srow[c]);
+                    else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(srow[c]);
+                }
+            }
         }
-        return;
-    }
-
-    // EPI_LAYER_IN: tile nt is one q head, one k head, one v head, or the gate logits
-    const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
-    if (nt < nk) {
-        float ss = 0.f;
-#pragma unroll
-        for (int c = 0; c < 64; ++c) ss = fmaf(srow[c], srow[c], ss);
-        ss += __shfl_xor(ss, 1, 64);
-        const bool is_q = nt < nq;
-        const float scale = (is_q ? p.q_scale : 1.f) / sqrtf(ss + 1e-6f);
-        if (!valid) return;
-        const int head = is_q ? nt : nt - nq;
-        bf16* dst = (is_q ? p.q : p.k) + (grow * p.Hqk + head) * 128 + 64 * half;
-#pragma unroll
-        for (int c = 0; c < 64; c += 8) {
-            bf16x8 ov;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] = (bf16)(srow[c + e] * scale);
-            *reinterpret_cast<bf16x8*>(dst + c) = ov;
-        }
-    } else if (nt < nv) {
-        if (!valid) return;
-        bf16* dst = p.v + (grow * p.Hv + (nt - nk)) * 128 + 64 * half;
-#pragma unroll
-        for (int c = 0; c < 64; c += 8) {
-            bf16x8 ov;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] = (bf16)srow[c + e];
-            *reinterpret_cast<bf16x8*>(dst + c) = ov;
-        }
-    } else {
-        if (!valid) return;
-        // columns [0, Hv) are the gate logits z_a, [Hv, 2 Hv) the write logits z_b
-        for (int c = 64 * half; c < 64 * half + 64 && c < 2 * p.Hv; ++c) {
-            const float z = stage[row][c];
-            if (c < p.Hv) p.g[grow * p.Hv + c] = -softplus_f(z);
-            else p.beta[grow * p.Hv + (c - p.Hv)] = sigmoid_f(z);
-        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
 }
 
 unsigned grid_for(int tiles) { return (unsigned)(((tiles + 7) / 8) * 8); }
+
+template <int EPI>
+hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
+    const hipError_t e = hipFuncSetAttribute((const void*)gemm_tn_kernel<EPI>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    const int tiles = p.G * p.n_mt * p.n_nt;
+    hipLaunchKernelGGL(gemm_tn_kernel<EPI>, dim3(grid_for(tiles)), dim3(NTHREADS), SMEM_BYTES, stream, p);
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -275,12 +327,11 @@ hipError_t launch_layer_in_gemm(const bf16* y, const PtrTable& w_qk, const PtrTa
     p.n0 = 2 * Hqk * 128; p.n1 = Hv * 128; p.n2 = Hv; p.n3 = Hv;
     p.G = G; p.M = n; p.K = d; p.N = p.n0 + p.n1 + p.n2 + p.n3;
     p.n_mt = (n + BM - 1) / BM;
-    p.n_nt = 2 * Hqk + Hv + 1;       // one tile per head, plus one for the 2 Hv gate columns
+    // 128-column segments: one per head, plus one for the 2 Hv gate columns; two per tile
+    p.n_nt = (2 * Hqk + Hv + 1 + 1) / 2;
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.Hqk = Hqk; p.Hv = Hv;
     p.q_scale = 1.0f / sqrtf(128.0f);
-    const int tiles = G * p.n_mt * p.n_nt;
-    hipLaunchKernelGGL(gemm_tn_kernel<EPI_LAYER_IN>, dim3(grid_for(tiles)), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    return launch_gemm<EPI_LAYER_IN>(p, stream);
 }
 
 hipError_t launch_out_residual_gemm(const bf16* o, const PtrTable& w_o, int G, int n, int din, int d,
@@ -289,11 +340,9 @@ hipError_t launch_out_residual_gemm(const bf16* o, const PtrTable& w_o, int G, i
     p.A = o; p.b0 = w_o; p.n0 = d;
     p.G = G; p.M = n; p.K = din; p.N = d;
     p.n_mt = (n + BM - 1) / BM;
-    p.n_nt = d / BN;
+    p.n_nt = (d + BN - 1) / BN;
     p.x_in = x_in; p.x_out = x_out;
-    const int tiles = G * p.n_mt * p.n_nt;
-    hipLaunchKernelGGL(gemm_tn_kernel<EPI_RESIDUAL>, dim3(grid_for(tiles)), dim3(256), 0, stream, p);
-    return hipGetLastError();
+    return launch_gemm<EPI_RESIDUAL>(p, stream);
 }
 
 }  // namespace tr
