@@ -20,6 +20,7 @@ events on the stream the kernel runs on.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -28,6 +29,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "gemm_tn_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
+    "rmsnorm_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
+    "gdn_chunk_bf16_kernel": "linear_attention_state_amd/csrc/gdn_chunk_bf16.hip",
+}
+COPY_BYTES = 1 << 30
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "replayed token-heads/sec (GDN state rebuild)"
 
@@ -44,7 +53,47 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline sample time")
     p.add_argument("--flush-cache", action="store_true",
                    help="write 512 MiB between steps so no input is cache-resident (timed per launch)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (the reference kernel for the "
+                        "FETCH_SIZE / WRITE_SIZE counter scale) and exit")
     return p.parse_args()
+
+
+# ---------------------------------------------------------------- HBM traffic
+def _sha256(path):
+    import hashlib
+    with open(os.path.join(HERE, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel_name, workload):
+    """HBM bytes per launch of a kernel from rocprofv3 FETCH_SIZE and WRITE_SIZE counts
+    (profiles/hbm_traffic.json), each scaled by the factor that turns the same counter's
+    reading for a plain copy of known size into that size.  None when no count exists, or
+    when the kernel's source has changed since the counts were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = kernel_name.split(" (")[0] + "@" + workload
+    ent = table.get("kernels", {}).get(key)
+    if not ent:
+        return None
+    src = KERNEL_SOURCES.get(key.split("<")[0].split("@")[0])
+    if src is None or ent.get("source_sha256") != _sha256(src):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 # ---------------------------------------------------------------- counting rules
@@ -139,14 +188,19 @@ def time_steps(step, steps, warmup, flush):
     stream = torch.cuda.current_stream()
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
     if not flush:
-        t_host = time.perf_counter()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        host_ms = (time.perf_counter() - t_host) * 1e3
+        gc.collect()
+        gc.disable()
+        try:
+            t_host = time.perf_counter()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            host_ms = (time.perf_counter() - t_host) * 1e3
+        finally:
+            gc.enable()
         return e0.elapsed_time(e1) / steps, host_ms / steps, None
     per = []
     for _ in range(steps):
@@ -168,16 +222,28 @@ def time_launches(fn, steps, warmup):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    # One untimed launch first: the GPU is then busy when the first start event is enqueued,
-    # so no event pair spans host-side gaps on an idle stream.
-    fn()
-    for a, b in ev:
-        a.record(stream)
+    # The GPU is kept busy while the launches are enqueued (a spin kernel first, and no
+    # garbage collection meanwhile), so no event pair spans a host-side pause on an idle stream.
+    gc.collect()
+    gc.disable()
+    try:
+        _busy_gpu(torch, 0.05)
         fn()
-        b.record(stream)
-    torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     d = [a.elapsed_time(b) for a, b in ev]
     return float(np.mean(d)), float(np.median(d)), float(np.min(d))
+
+
+def _busy_gpu(torch, seconds):
+    """Enqueue about `seconds` of GPU spinning on the current stream."""
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(seconds * 2.4e9))
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -238,6 +304,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import linear_attention_state_amd as tr
     tr.lib()   # fails loudly if the HIP library is not built
 
@@ -259,8 +328,9 @@ def main():
         def kern():
             gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_host, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
         k_mean, k_med, k_min = time_launches(kern, max(args.steps, 10), 2)
+        kname = "gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"])
         roof = dict(bound="hbm", achieved=nbytes / (k_mean * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                    traffic=None, kernel="gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"]),
+                    traffic=measured_traffic(kname, args.workload), kernel=kname,
                     algorithmic_bytes=nbytes, avg_launch_us=k_mean * 1e3, median_launch_us=k_med * 1e3,
                     min_launch_us=k_min * 1e3)
         roof["frac"] = roof["achieved"] / roof["peak"]
@@ -368,7 +438,8 @@ def group_roofline(w, args):
     else:
         roof = dict(bound="hbm", achieved=top["achieved_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     algorithmic_bytes=top["work"])
-    roof.update(frac=roof["achieved"] / roof["peak"], traffic=None, kernel=name, avg_launch_us=top["avg_us"],
+    roof.update(frac=roof["achieved"] / roof["peak"], traffic=measured_traffic(name, args.workload),
+                kernel=name, avg_launch_us=top["avg_us"],
                 kernels={k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()
                              if kk != "work"} for k, v in kernels.items()})
     return roof

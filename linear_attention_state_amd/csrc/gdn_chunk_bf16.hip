@@ -205,8 +205,14 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     int tr_p = (lane & 15) >> 2;
     int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    const int b = blockIdx.x / Hv;
-    const int hv = blockIdx.x % Hv;
+    // Workgroup order: consecutive work items (the value heads that share a query/key head
+    // come next to each other) go to one XCD (blockIdx % 8 picks the XCD), so the second
+    // reader of each key/query tile finds it in that XCD's L2.
+    const int per_xcd = (int)(gridDim.x / 8);
+    const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (item >= B * Hv) return;
+    const int b = item / Hv;
+    const int hv = item % Hv;
     const int hq = hv / (Hv / Hqk);
     const int bos = cu ? cu[b] : b * uniform_len;
     const int len = cu ? cu[b + 1] - bos : uniform_len;
@@ -657,7 +663,7 @@ hipError_t launch(const GdnArgs& a, hipStream_t stream) {
     const size_t smem = sizeof(Smem<DK, DV>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)(a.B * a.Hv));
+    const dim3 grid((unsigned)((a.B * a.Hv + 7) / 8 * 8));    // a multiple of 8: one share per XCD
     const dim3 block(DV * 2);
     hipLaunchKernelGGL(kern, grid, block, smem, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
