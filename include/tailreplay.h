@@ -114,6 +114,90 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * tr_gdn_transition -- the product of the transition operators of a replayed span.
+ *
+ * For every sequence b and value head h, over the n tokens of sequence b, computes
+ *     Phi[b, h] = T_1 T_2 ... T_n,   T_t = alpha_t (I - beta_t k_t k_t^T):
+ * the recurrence of tr_gdn_replay started from S = I with all values zero.  By the linearity
+ * of the recurrence in its start (reading notes, section 2.3: S_m splits into the start
+ * carried through the operators plus the replayed part from zero), a state S_a before the
+ * span continues as
+ *     S_m = S_a Phi + S_hat_m,
+ * where S_hat_m is tr_gdn_replay of the span from zero; so E_m = S_a Phi is exactly the
+ * error of replaying from zero, and Phi composes checkpoints (tr_state_compose).
+ *
+ * The decays multiply to exp(sum g), which leaves the fp32 range after a few thousand
+ * tokens at typical gates.  With log_scale_out non-NULL the decay is kept apart:
+ *     phi_out = (I - beta_1 k_1 k_1^T) ... (I - beta_n k_n k_n^T),  log_scale_out = sum_t g_t,
+ * and Phi = exp(log_scale_out) phi_out.  With log_scale_out NULL, phi_out = Phi directly.
+ *
+ * Arguments
+ *   k, g, beta, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, dt
+ *                 as for tr_gdn_replay (no q and no v: they do not enter Phi)
+ *   d             dk = dv = d, in {64, 128}
+ *   phi_out       [device] [B, Hv, d, d] fp32 (row-major)
+ *   log_scale_out [device] [B, Hv] fp32, or NULL (see above)
+ *   stream        hipStream_t to enqueue on
+ * Arithmetic is fp32 token by token for both input types (bf16 keys are converted
+ * exactly): a long product of operators keeps every rounding it meets, so the chunked bf16
+ * path is not used here.  An empty sequence gives phi_out = I (and log scale 0).
+ * Errors: as for tr_gdn_replay.
+ * ------------------------------------------------------------------------------- */
+tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
+                            const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                            int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t d,
+                            tr_dtype dt, float* phi_out, float* log_scale_out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * tr_state_compose -- out[n] = exp(log_scale[n]) S_c[n] phi[n] + S_hat[n] for n < N.
+ *
+ * The composition of reading notes section 2.3 (start carried through the span plus the
+ * replayed part): with S_c a state before a span, exp(log_scale) phi its transition product
+ * (tr_gdn_transition) and S_hat its replay from zero (tr_gdn_replay), out is the state after
+ * the span; with S_hat NULL, out is the carried start alone (the exact truncation error
+ * E_m = S_a Phi).
+ *
+ * Arguments
+ *   S_c       [device] [N, dv, dk] fp32
+ *   phi       [device] [N, dk, dk] fp32
+ *   log_scale [device] [N] fp32, or NULL for 0 (phi is then the whole product)
+ *   S_hat     [device] [N, dv, dk] fp32, or NULL for zero
+ *   out       [device] [N, dv, dk] fp32; may equal S_hat, must not overlap S_c or phi
+ *   N         >= 1 matrices; dv, dk in {64, 128}
+ *   stream    hipStream_t to enqueue on
+ * fp32 arithmetic; a scale below the fp32 range makes the carried term zero.  Errors:
+ * TR_ERR_INVALID_ARG (N < 1, null pointers, forbidden aliasing), TR_ERR_UNSUPPORTED (sizes),
+ * TR_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+tr_status tr_state_compose(const float* S_c, const float* phi, const float* log_scale, const float* S_hat,
+                           float* out, int32_t N, int32_t dv, int32_t dk, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * tr_gdn_decode -- one recurrence step per (sequence, value head) on resident states.
+ *
+ * For every b < B and value head h (query/key head h / (Hv / Hqk)), in place:
+ *     S[b, h] <- alpha S[b, h] (I - beta k k^T) + beta v k^T,   alpha = exp(g[b, h]),
+ *     o[b, h]  = S[b, h] (q_scale q)
+ * Reading notes, section 2.3, Eq. (1) for one token; after a replay the suffix continues
+ * from the rebuilt state (section 2.2, step 4), one token at a time when decoding.
+ *
+ * Arguments
+ *   q, k    [device] [B, Hqk, dk] dtype dt
+ *   v       [device] [B, Hv, dv]  dtype dt
+ *   g, beta [device] [B, Hv] fp32
+ *   B, Hqk, Hv, dk, dv   sizes; Hv % Hqk == 0; dk, dv in {64, 128}
+ *   dt      TR_BF16 or TR_F32 (inputs and o; the state and the arithmetic are fp32)
+ *   q_scale > 0
+ *   state   [device] [B, Hv, dv, dk] fp32, read and overwritten
+ *   o       [device] [B, Hv, dv] dtype dt, or NULL
+ *   stream  hipStream_t to enqueue on
+ * Errors: TR_ERR_INVALID_ARG, TR_ERR_UNSUPPORTED, TR_ERR_HIP.
+ * ------------------------------------------------------------------------------- */
+tr_status tr_gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                        int32_t B, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, tr_dtype dt, float q_scale,
+                        float* state, void* o, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * One LA layer's weights, all [device] bf16, row-major [out, in]:
  *   w_qk [2*Hqk*dk, d_model]   query heads first, then key heads
  *   w_v  [Hv*dv,    d_model]

@@ -35,6 +35,11 @@ SIGNATURES = {
     "tr_gdn_replay": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
                                      _vp, _vp, _vp, _vp]),
+    "tr_gdn_transition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                         _vp, _vp, _vp]),
+    "tr_state_compose": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "tr_gdn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
+                                     _vp, _vp, _vp]),
     "tr_la_layer_inputs_workspace_size": (_sz, [_i32, _i32, _i32]),
     "tr_la_layer_inputs": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

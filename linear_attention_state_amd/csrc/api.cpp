@@ -183,6 +183,45 @@ tr_status tr_tail_seqlens(const int64_t* m_host, int32_t B, int32_t r_num, int32
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks of the varlen recurrence entry points; sets *max_len.
+tr_status check_gdn(const char* fn, const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                    int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, tr_dtype dt,
+                    int32_t* max_len) {
+    if (B < 1) return fail(TR_ERR_INVALID_ARG, "%s: B = %d, need B >= 1", fn, B);
+    if (T < 0) return fail(TR_ERR_INVALID_ARG, "%s: T = %d is negative", fn, T);
+    if (Hqk < 1 || Hv < 1) return fail(TR_ERR_INVALID_ARG, "%s: head counts must be >= 1 (Hqk=%d, Hv=%d)", fn, Hqk, Hv);
+    if (Hv % Hqk != 0) return fail(TR_ERR_INVALID_ARG, "%s: Hv = %d is not a multiple of Hqk = %d", fn, Hv, Hqk);
+    if (dt != TR_BF16 && dt != TR_F32) return fail(TR_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+    if (!supported_head_dim(dk) || !supported_head_dim(dv))
+        return fail(TR_ERR_UNSUPPORTED, "%s: dk = %d, dv = %d; supported head dims are 64 and 128", fn, dk, dv);
+    if ((int64_t)B * Hv > INT32_MAX) return fail(TR_ERR_INVALID_ARG, "%s: B * Hv too large", fn);
+    if (!cu_seqlens_host || !cu_seqlens_dev) return fail(TR_ERR_INVALID_ARG, "%s: null cu_seqlens", fn);
+    if (cu_seqlens_host[0] != 0) return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens[0] = %d, must be 0", fn, cu_seqlens_host[0]);
+    int32_t ml = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t l = cu_seqlens_host[b + 1] - cu_seqlens_host[b];
+        if (cu_seqlens_host[b + 1] < cu_seqlens_host[b])
+            return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens decreases at %d", fn, b + 1);
+        if (l > ml) ml = l;
+    }
+    if (cu_seqlens_host[B] != T)
+        return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens[B] = %d but T = %d", fn, cu_seqlens_host[B], T);
+    *max_len = ml;
+    return TR_OK;
+}
+
+hipError_t launch_gdn(const tr::GdnArgs& a, tr_dtype dt, hipStream_t s) {
+    return (dt == TR_BF16) ? tr::launch_gdn_chunk_bf16(a, s) : tr::launch_gdn_token_f32(a, s);
+}
+
+}  // namespace
+
+extern "C" {
+
 tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         const float* g, const float* beta,
                         const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
@@ -191,8 +230,66 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         const float* state_in, float* state_out, void* o,
                         void* stream) {
     static const char* fn = "tr_gdn_replay";
+    int32_t max_len = 0;
+    const tr_status st = check_gdn(fn, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, dk, dv, dt, &max_len);
+    if (st != TR_OK) return st;
+    if (!(q_scale > 0.f) || !std::isfinite(q_scale))
+        return fail(TR_ERR_INVALID_ARG, "%s: q_scale must be finite and > 0", fn);
+    if (!state_out) return fail(TR_ERR_INVALID_ARG, "%s: null state_out", fn);
+    if (T > 0 && (!q || !k || !v || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
+
+    tr::GdnArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens_dev;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = q_scale;
+    a.state_in = state_in; a.state_identity = 0; a.state_out = state_out; a.o = o; a.max_len = max_len;
+    a.log_scale_out = nullptr;
+    a.uniform_len = 0; a.state_bstride = (int64_t)Hv * dv * dk;
+    hipStream_t s = (hipStream_t)stream;
+    return finish_launch(launch_gdn(a, dt, s), s, fn);
+}
+
+tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
+                            const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                            int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t d,
+                            tr_dtype dt, float* phi_out, float* log_scale_out, void* stream) {
+    static const char* fn = "tr_gdn_transition";
+    int32_t max_len = 0;
+    const tr_status st = check_gdn(fn, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, d, d, dt, &max_len);
+    if (st != TR_OK) return st;
+    if (!phi_out) return fail(TR_ERR_INVALID_ARG, "%s: null phi_out", fn);
+    if (T > 0 && (!k || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
+
+    // The recurrence from S = I with zero values: S_m = I T_{a+1} ... T_m, in fp32 arithmetic
+    // for either input type (a product of many operators keeps every rounding it meets).
+    tr::GdnArgs a;
+    a.q = nullptr; a.k = k; a.v = nullptr; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens_dev;
+    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = d; a.dv = d; a.q_scale = 1.f;
+    a.state_in = nullptr; a.state_identity = 1; a.state_out = phi_out; a.o = nullptr; a.max_len = max_len;
+    a.log_scale_out = log_scale_out;
+    a.uniform_len = 0; a.state_bstride = (int64_t)Hv * d * d;
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_token_f32_bf16in(a, s) : tr::launch_gdn_token_f32(a, s);
+    return finish_launch(e, s, fn);
+}
+
+tr_status tr_state_compose(const float* S_c, const float* phi, const float* log_scale, const float* S_hat,
+                           float* out, int32_t N, int32_t dv, int32_t dk, void* stream) {
+    static const char* fn = "tr_state_compose";
+    if (N < 1) return fail(TR_ERR_INVALID_ARG, "%s: N = %d, need N >= 1", fn, N);
+    if (!supported_head_dim(dk) || !supported_head_dim(dv))
+        return fail(TR_ERR_UNSUPPORTED, "%s: dk = %d, dv = %d; supported head dims are 64 and 128", fn, dk, dv);
+    if (!S_c || !phi || !out) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (out == S_c || out == phi) return fail(TR_ERR_INVALID_ARG, "%s: out may alias only S_hat", fn);
+    if ((int64_t)N * (dv / 64) * (dk / 64) > INT32_MAX) return fail(TR_ERR_INVALID_ARG, "%s: N too large", fn);
+    hipStream_t s = (hipStream_t)stream;
+    return finish_launch(tr::launch_state_compose(S_c, phi, log_scale, S_hat, out, N, dv, dk, s), s, fn);
+}
+
+tr_status tr_gdn_decode(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                        int32_t B, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, tr_dtype dt, float q_scale,
+                        float* state, void* o, void* stream) {
+    static const char* fn = "tr_gdn_decode";
     if (B < 1) return fail(TR_ERR_INVALID_ARG, "%s: B = %d, need B >= 1", fn, B);
-    if (T < 0) return fail(TR_ERR_INVALID_ARG, "%s: T = %d is negative", fn, T);
     if (Hqk < 1 || Hv < 1) return fail(TR_ERR_INVALID_ARG, "%s: head counts must be >= 1 (Hqk=%d, Hv=%d)", fn, Hqk, Hv);
     if (Hv % Hqk != 0) return fail(TR_ERR_INVALID_ARG, "%s: Hv = %d is not a multiple of Hqk = %d", fn, Hv, Hqk);
     if (dt != TR_BF16 && dt != TR_F32) return fail(TR_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
@@ -201,28 +298,13 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     if (!(q_scale > 0.f) || !std::isfinite(q_scale))
         return fail(TR_ERR_INVALID_ARG, "%s: q_scale must be finite and > 0", fn);
     if ((int64_t)B * Hv > INT32_MAX) return fail(TR_ERR_INVALID_ARG, "%s: B * Hv too large", fn);
-    if (!cu_seqlens_host || !cu_seqlens_dev) return fail(TR_ERR_INVALID_ARG, "%s: null cu_seqlens", fn);
-    if (!state_out) return fail(TR_ERR_INVALID_ARG, "%s: null state_out", fn);
-    if (T > 0 && (!q || !k || !v || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
-    if (cu_seqlens_host[0] != 0) return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens[0] = %d, must be 0", fn, cu_seqlens_host[0]);
-    int32_t max_len = 0;
-    for (int32_t b = 0; b < B; ++b) {
-        const int32_t l = cu_seqlens_host[b + 1] - cu_seqlens_host[b];
-        if (cu_seqlens_host[b + 1] < cu_seqlens_host[b])
-            return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens decreases at %d", fn, b + 1);
-        if (l > max_len) max_len = l;
-    }
-    if (cu_seqlens_host[B] != T)
-        return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens[B] = %d but T = %d", fn, cu_seqlens_host[B], T);
-
-    tr::GdnArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens_dev;
-    a.B = B; a.T = T; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = q_scale;
-    a.state_in = state_in; a.state_out = state_out; a.o = o; a.max_len = max_len;
-    a.uniform_len = 0; a.state_bstride = (int64_t)Hv * dv * dk;
+    if (!q || !k || !v || !g || !beta || !state) return fail(TR_ERR_INVALID_ARG, "%s: null pointer", fn);
+    tr::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.B = B; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.is_bf16 = dt == TR_BF16; a.q_scale = q_scale;
+    a.state = state; a.o = o;
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_chunk_bf16(a, s) : tr::launch_gdn_token_f32(a, s);
-    return finish_launch(e, s, fn);
+    return finish_launch(tr::launch_gdn_decode(a, s), s, fn);
 }
 
 size_t tr_la_layer_inputs_workspace_size(int32_t G, int32_t n_tokens, int32_t d_model) {
@@ -352,6 +434,8 @@ tr_status tr_group_replay(const void* h_tail, const tr_la_weights* w,
         if (e != hipSuccess) return finish_launch(e, s, fn);
         // the recurrence from the zero state; the last layer keeps its state only
         tr::GdnArgs a;
+        a.state_identity = 0;
+        a.log_scale_out = nullptr;
         a.q = qbuf; a.k = kbuf; a.v = vbuf; a.g = gbuf; a.beta = bbuf;
         a.cu_seqlens = nullptr; a.uniform_len = n_tokens;
         a.B = G; a.T = G * n_tokens; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = 1.0f;

@@ -178,7 +178,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
                       int B, int Hqk, int Hv, float q_scale, int uniform_len, long long state_bstride,
-                      const float* state_in, float* state_out, bf16* __restrict__ o)
+                      const float* state_in, int state_identity, float* state_out, bf16* __restrict__ o)
 {
     constexpr int NW = DV / 32;            // waves; wave w owns dv columns [32w, 32w+32)
     constexpr int NT = NW * 64;
@@ -224,8 +224,9 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t v_stride = (uint32_t)Hv * DV * 2;
     const uint32_t gb_stride = (uint32_t)Hv * 4;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + ((size_t)bos * Hqk + hq) * DK, (uint32_t)len * kq_stride);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + ((size_t)bos * Hqk + hq) * DK, (uint32_t)len * kq_stride);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + ((size_t)bos * Hv + hv) * DV, (uint32_t)len * v_stride);
+    // a null q or v reads as zeros (empty resource)
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q ? q + ((size_t)bos * Hqk + hq) * DK : nullptr, q ? (uint32_t)len * kq_stride : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v ? v + ((size_t)bos * Hv + hv) * DV : nullptr, v ? (uint32_t)len * v_stride : 0u);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
     // outputs: stores past the sequence end fall outside the resource and are dropped
@@ -236,7 +237,14 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const size_t sbase = (size_t)b * state_bstride + (size_t)hv * DV * DK + (size_t)(col0 + l32) * DK;
 #pragma unroll
     for (int r = 0; r < KT_TILES; ++r) {
-        if (state_in) {
+        if (state_identity) {
+            // S = I: element (dv col0 + l32, dk 32 r + 8 q4 + 4 h2 + i)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    St[r][4 * q4 + i] = (32 * r + 8 * q4 + 4 * h2 + i == col0 + l32) ? 1.f : 0.f;
+        } else if (state_in) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(state_in + sbase + 32 * r + 8 * q4 + 4 * h2);
@@ -668,7 +676,7 @@ hipError_t launch(const GdnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, grid, block, smem, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
                        a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
-                       a.state_in, a.state_out, (bf16*)a.o);
+                       a.state_in, a.state_identity, a.state_out, (bf16*)a.o);
     return hipGetLastError();
 }
 

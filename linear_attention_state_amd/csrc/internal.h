@@ -20,15 +20,37 @@ struct GdnArgs {
     int32_t B, T, Hqk, Hv, dk, dv;
     float q_scale;
     const float* state_in;       // may be null (zero state)
+    int32_t state_identity;      // 1: start every (sequence, head) from I (dk == dv); state_in unused
+    float* log_scale_out;        // non-null (fp32 token path only): run with alpha = 1 and write
+                                 // sum(g) per (sequence, head) here, [B, Hv]
     float* state_out;
     void* o;                     // may be null (state-only)
     int32_t max_len;             // longest sequence (host-computed)
+    // v may be null: every value vector is zero.  q may be null when o is null.
 };
 
 // Chunked WY-form recurrence, bf16 operands, fp32 state (gdn_chunk_bf16.hip).
 hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream);
 // Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
 hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream);
+// The same fp32 arithmetic on bf16 inputs (and bf16 outputs).
+hipError_t launch_gdn_token_f32_bf16in(const GdnArgs& a, hipStream_t stream);
+
+// State algebra and single-token steps (state_ops.hip).
+// out[n] = exp(log_scale[n]) S_c[n] Phi[n] (+ S_hat[n]) for n < N (log_scale may be null); S_c, S_hat, out [N, dv, dk], Phi [N, dk, dk], fp32.
+hipError_t launch_state_compose(const float* S_c, const float* Phi, const float* log_scale, const float* S_hat,
+                                float* out, int N, int dv, int dk, hipStream_t stream);
+// One recurrence step per (sequence, value head) on a resident state, in place.
+struct DecodeArgs {
+    const void* q; const void* k; const void* v;   // [B, Hqk, dk], [B, Hqk, dk], [B, Hv, dv]
+    const float* g; const float* beta;             // [B, Hv]
+    int32_t B, Hqk, Hv, dk, dv;
+    int32_t is_bf16;
+    float q_scale;
+    float* state;                                  // [B, Hv, dv, dk], updated in place
+    void* o;                                       // [B, Hv, dv] or null
+};
+hipError_t launch_gdn_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Group path (la_layer.hip).  Per-group weight pointers travel in kernel arguments.
 constexpr int kMaxGroupsPerLaunch = 16;

@@ -85,6 +85,75 @@ def gdn_replay(q, k, v, g, beta, cu_seqlens, q_scale: float = 1.0, state_in=None
     return state_out, o
 
 
+def gdn_transition(k, g, beta, cu_seqlens, cu_seqlens_dev=None, phi_out=None, separate_decay: bool = False,
+                   stream=None):
+    """Transition products of the packed spans (tr_gdn_transition): the recurrence from S = I
+    with zero values.  k [T, Hqk, d] bf16 or fp32; g, beta [T, Hv] fp32.  Returns Phi
+    [B, Hv, d, d], or with separate_decay (phi, log_scale [B, Hv]) where Phi = exp(log_scale) phi."""
+    _need(k.is_cuda and g.is_cuda and beta.is_cuda, "inputs must be on the GPU")
+    _need(k.dtype in _DT and g.dtype == torch.float32 and beta.dtype == torch.float32, "dtypes")
+    for t in (k, g, beta):
+        _need(t.is_contiguous(), "inputs must be contiguous")
+    _need(k.dim() == 3, "k: [T, Hqk, d]")
+    T, Hqk, d = k.shape
+    _need(g.dim() == 2 and g.shape[0] == T and beta.shape == g.shape, "g, beta: [T, Hv]")
+    Hv = g.shape[1]
+    cu = cu_seqlens.to(torch.int32).cpu().contiguous()
+    B = cu.numel() - 1
+    if cu_seqlens_dev is None:
+        cu_seqlens_dev = cu.to(k.device)
+    if phi_out is None:
+        phi_out = torch.empty((B, Hv, d, d), dtype=torch.float32, device=k.device)
+    _need(phi_out.is_cuda and phi_out.dtype == torch.float32 and phi_out.is_contiguous()
+          and tuple(phi_out.shape) == (B, Hv, d, d), "phi_out must be [B, Hv, d, d] fp32")
+    log_scale = torch.empty((B, Hv), dtype=torch.float32, device=k.device) if separate_decay else None
+    check(lib().tr_gdn_transition(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu), _ptr(cu_seqlens_dev),
+                                  B, T, Hqk, Hv, d, _DT[k.dtype], _ptr(phi_out), _ptr(log_scale), _stream(stream)))
+    return (phi_out, log_scale) if separate_decay else phi_out
+
+
+def state_compose(S_c, phi, S_hat=None, out=None, log_scale=None, stream=None):
+    """out = exp(log_scale) S_c @ phi (+ S_hat) over the leading dimensions (tr_state_compose), fp32."""
+    _need(S_c.is_cuda and S_c.dtype == torch.float32 and S_c.is_contiguous(), "S_c: fp32 contiguous on the GPU")
+    dv, dk = S_c.shape[-2], S_c.shape[-1]
+    N = S_c.numel() // (dv * dk)
+    _need(phi.is_cuda and phi.dtype == torch.float32 and phi.is_contiguous()
+          and tuple(phi.shape) == tuple(S_c.shape[:-2]) + (dk, dk), "phi: [..., dk, dk] fp32")
+    if S_hat is not None:
+        _need(S_hat.is_cuda and S_hat.dtype == torch.float32 and S_hat.is_contiguous()
+              and S_hat.shape == S_c.shape, "S_hat: same shape as S_c")
+    if log_scale is not None:
+        _need(log_scale.is_cuda and log_scale.dtype == torch.float32 and log_scale.is_contiguous()
+              and log_scale.numel() == N, "log_scale: one fp32 per matrix")
+    if out is None:
+        out = torch.empty_like(S_c)
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.shape == S_c.shape, "out")
+    check(lib().tr_state_compose(_ptr(S_c), _ptr(phi), _ptr(log_scale), _ptr(S_hat), _ptr(out), N, dv, dk,
+                                 _stream(stream)))
+    return out
+
+
+def gdn_decode(q, k, v, g, beta, state, q_scale: float = 1.0, want_o: bool = True, o=None, stream=None):
+    """One recurrence step per (sequence, value head), state updated in place (tr_gdn_decode).
+    q, k [B, Hqk, dk], v [B, Hv, dv] bf16 or fp32; g, beta [B, Hv] fp32; state [B, Hv, dv, dk]."""
+    _need(q.is_cuda and k.is_cuda and v.is_cuda and g.is_cuda and beta.is_cuda and state.is_cuda, "GPU tensors")
+    _need(q.dtype == k.dtype == v.dtype and q.dtype in _DT, "q, k, v must share dtype bf16 or fp32")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32 and state.dtype == torch.float32, "fp32")
+    for t in (q, k, v, g, beta, state):
+        _need(t.is_contiguous(), "inputs must be contiguous")
+    B, Hqk, dk = q.shape
+    _, Hv, dv = v.shape
+    _need(k.shape == q.shape and v.shape[0] == B and g.shape == (B, Hv) and beta.shape == (B, Hv)
+          and tuple(state.shape) == (B, Hv, dv, dk), "shape mismatch")
+    if want_o and o is None:
+        o = torch.empty((B, Hv, dv), dtype=q.dtype, device=q.device)
+    if not want_o:
+        o = None
+    check(lib().tr_gdn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), B, Hqk, Hv, dk, dv,
+                              _DT[q.dtype], float(q_scale), _ptr(state), _ptr(o), _stream(stream)))
+    return o
+
+
 def _weights_struct(w: dict) -> LaWeights:
     return LaWeights(w["w_qk"].data_ptr(), w["w_v"].data_ptr(), w["w_a"].data_ptr(), w["w_b"].data_ptr(),
                      w["w_o"].data_ptr() if w.get("w_o") is not None else None,

@@ -95,3 +95,46 @@ def test_gdn_rejects_bad_cu_seqlens():
         cu = (ctypes.c_int32 * 3)(*bad)
         st, msg = call_gdn(cu_h=ctypes.cast(cu, ctypes.c_void_p), T=bad[-1])
         assert st == 1 and "cu_seqlens" in msg
+
+
+def call_transition(**over):
+    cu = (ctypes.c_int32 * 3)(0, 5, 9)
+    args = dict(k=FAKE, g=FAKE, beta=FAKE, cu_h=ctypes.cast(cu, ctypes.c_void_p), cu_d=FAKE,
+                B=2, T=9, Hqk=2, Hv=4, d=128, dt=0, phi=FAKE)
+    args.update(over)
+    lib = L.lib()
+    st = lib.tr_gdn_transition(args["k"], args["g"], args["beta"], args["cu_h"], args["cu_d"], args["B"], args["T"],
+                               args["Hqk"], args["Hv"], args["d"], args["dt"], args["phi"], None, None)
+    return st, lib.tr_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 1), (dict(Hv=3), 1), (dict(d=96), 2), (dict(dt=5), 1), (dict(k=None), 1),
+    (dict(phi=None), 1), (dict(cu_d=None), 1), (dict(T=8), 1),
+])
+def test_transition_rejects_bad_arguments(over, status):
+    st, msg = call_transition(**over)
+    assert st == status and "tr_gdn_transition" in msg
+
+
+def test_state_compose_rejects_bad_arguments():
+    lib = L.lib()
+    other = ctypes.c_void_p(0x2000)
+    cases = [((FAKE, FAKE, None, None, other, 0, 128, 128), 1),          # N < 1
+             ((FAKE, FAKE, None, None, other, 4, 96, 128), 2),           # unsupported dv
+             ((None, FAKE, None, None, other, 4, 128, 128), 1),          # null S_c
+             ((FAKE, other, None, None, FAKE, 4, 128, 128), 1),          # out aliases S_c
+             ((other, FAKE, None, None, FAKE, 4, 128, 128), 1)]          # out aliases phi
+    for args, status in cases:
+        st = lib.tr_state_compose(*args, None)
+        assert st == status and "tr_state_compose" in lib.tr_last_error().decode()
+
+
+def test_decode_rejects_bad_arguments():
+    lib = L.lib()
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 4, 128, 128, 0, 1.0, FAKE, FAKE, None]
+    for idx, val, status in [(5, 0, 1), (7, 3, 1), (8, 32, 2), (10, 9, 1), (11, -1.0, 1), (12, None, 1), (0, None, 1)]:
+        args = list(base)
+        args[idx] = val
+        st = lib.tr_gdn_decode(*args)
+        assert st == status and "tr_gdn_decode" in lib.tr_last_error().decode(), (idx, val)
