@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "gemm_tn_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
     "rmsnorm_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
     "gdn_chunk_bf16_kernel": "linear_attention_state_amd/csrc/gdn_chunk_bf16.hip",
+    "gdn_decode_kernel": "linear_attention_state_amd/csrc/state_ops.hip",
 }
 COPY_BYTES = 1 << 30
 BF16_PEAK_TFLOPS = 2500.0
@@ -47,7 +48,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="group",
-                   choices=["group", "batched_r05", "batched", "single_hit", "varlen"])
+                   choices=["group", "batched_r05", "batched", "single_hit", "varlen",
+                            "fidelity", "full_prefix", "decode", "overlap"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline sample time")
@@ -133,7 +135,7 @@ def build_workload(name, seed):
 
     spec = dict(synthetic.WORKLOADS[name])
     rn, rd = spec["r"]
-    if name == "group":
+    if "G" in spec:
         G, L = spec["G"], spec["L"]
         ms = [spec["m"]] * G
         cu, _ = tail_seqlens(ms, rn, rd)
@@ -277,20 +279,196 @@ def cpu_baseline(w, min_seconds):
     # group: whole groups (all layers) through the chain oracle
     spec, gi = w["spec"], w["inputs"]
     done_th, elapsed, units = 0, 0.0, 0
+    n_cpu = min(w["n"], 1639)       # a token prefix of each group is a whole replay of its own
     for g in range(spec["G"]):
-        h = np64(gi.h_tail[g:g + 1])
+        h = np64(gi.h_tail[g:g + 1, :n_cpu])
         ws = [[{k: np64(t) for k, t in d.items()} for d in gi.weights[g]]]
         t0 = time.perf_counter()
         oracle.group(h, ws, spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
         elapsed += time.perf_counter() - t0
-        done_th += w["n"] * spec["Hv"] * spec["L"]
+        done_th += n_cpu * spec["Hv"] * spec["L"]
         units += 1
         if elapsed >= min_seconds:
             break
     sample = "%d of %d groups x %d layers x %d heads x %d tokens, fp64" % (
-        units, spec["G"], spec["L"], spec["Hv"], w["n"])
+        units, spec["G"], spec["L"], spec["Hv"], n_cpu)
     return dict(value=done_th / elapsed, unit="token-heads/s", cores=oracle.num_threads(), kind="oracle",
                 sample=sample, seconds=round(elapsed, 2))
+
+
+# ---------------------------------------------------------------- next-row modes
+def _line(args, value, ms, config, roof, extra):
+    line = {"metric": METRIC, "value": value, "unit": "token-heads/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config, "roofline": roof}
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def run_fidelity(args):
+    """One 32,768-token sequence: the full recurrence from zero, the tail replays at each r,
+    and the transition products; reports |S_m - S_hat_m| / |S_m| and the exact truncation
+    |S_a Phi| / |S_m| (both from the GPU path), and the times."""
+    import torch
+    import synthetic
+    from linear_attention_state_amd import gdn_replay, gdn_transition, state_compose, tail_seqlens
+    spec = synthetic.WORKLOADS["fidelity"]
+    m, H, d = spec["m"], spec["Hv"], spec["dk"]
+    inp = synthetic.gdn_inputs([m], spec["Hqk"], H, d, d, seed=args.seed, backend="torch", device="cuda")
+    cu_m = torch.tensor([0, m], dtype=torch.int32)
+    cu_m_dev = cu_m.cuda()
+    S_m = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+
+    def full():
+        gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_m, cu_seqlens_dev=cu_m_dev, state_out=S_m, want_o=False)
+    t_full = time_launches(full, max(args.steps, 5), 1)[0]
+    res = {}
+    for rn, rd in spec["rs"]:
+        k = int(tail_seqlens([m], rn, rd)[0][1])
+        a = m - k
+        head = [t[:a].contiguous() for t in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
+        tail = [t[a:].contiguous() for t in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
+        cu_k = torch.tensor([0, k], dtype=torch.int32)
+        cu_k_dev = cu_k.cuda()
+        S_hat = torch.empty_like(S_m)
+
+        def replay():
+            gdn_replay(*tail, cu_k, cu_seqlens_dev=cu_k_dev, state_out=S_hat, want_o=False)
+        t_rep = time_launches(replay, max(args.steps, 5), 1)[0]
+        psi = torch.empty_like(S_m)
+
+        def transition():
+            return gdn_transition(tail[1], tail[3], tail[4], cu_k, cu_seqlens_dev=cu_k_dev, phi_out=psi,
+                                  separate_decay=True)
+        t_phi = time_launches(transition, 3, 1)[0]
+        _, ls = transition()
+        S_a, _ = gdn_replay(*head, torch.tensor([0, a], dtype=torch.int32), want_o=False)
+        E = state_compose(S_a, psi)                       # S_a psi; Phi = exp(ls) psi
+        torch.cuda.synchronize()
+        nm = torch.linalg.matrix_norm(S_m[0].double())
+        measured = (torch.linalg.matrix_norm((S_m[0] - S_hat[0]).double()) / nm).cpu().numpy()
+        log10_exact = ((ls[0].double() + torch.log(torch.linalg.matrix_norm(E[0].double())) - torch.log(nm))
+                       / np.log(10)).cpu().numpy()
+        res["r=%d/%d" % (rn, rd)] = dict(
+            tail_tokens=k, replay_us=t_rep * 1e3, transition_us=t_phi * 1e3,
+            rel_state_error_max=float(measured.max()), rel_state_error_mean=float(measured.mean()),
+            log10_exact_truncation_max=float(log10_exact.max()))
+    nbytes = gdn_bytes(m, 1, spec["Hqk"], H, d, d, with_o=False)
+    roof = dict(bound="hbm", achieved=nbytes / (t_full * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                traffic=None, kernel="gdn_chunk_bf16_kernel<128,128> (state only, one 32768-token sequence)",
+                algorithmic_bytes=nbytes, avg_launch_us=t_full * 1e3)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    config = dict(workload="fidelity", tokens=m, Hqk=spec["Hqk"], Hv=H, dk=d, dv=d, chunk=64,
+                  rs=["%d/%d" % r for r in spec["rs"]])
+    _line(args, m * H / (t_full * 1e-3), t_full, config, roof,
+          {"fidelity": res, "note": "value: the full-prefix recurrence of the sequence (state only); "
+           "rel_state_error = |S_m - S_hat_m|_F / |S_m|_F per head, GPU path; the exact truncation "
+           "|S_a Phi|_F / |S_m|_F from tr_gdn_transition and tr_state_compose, in log10"})
+
+
+def run_decode(args):
+    import torch
+    import synthetic
+    from linear_attention_state_amd import gdn_decode
+    spec = synthetic.WORKLOADS["decode"]
+    B, Hqk, Hv, dk, dv = spec["B"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"]
+    inp = synthetic.gdn_inputs([1] * B, Hqk, Hv, dk, dv, seed=args.seed, backend="torch", device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+    state = torch.randn((B, Hv, dv, dk), generator=gen, device="cuda") * 0.1
+    o = torch.empty((B, Hv, dv), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        gdn_decode(inp.q, inp.k, inp.v, inp.g, inp.beta, state, o=o)
+    ms, _, _ = time_steps(step, args.steps, args.warmup, False)
+    t_mean, t_med, t_min = time_launches(step, max(args.steps, 10), 2)
+    nbytes = B * Hv * dv * dk * 4 * 2 + B * (Hqk * dk * 2 * 2 + Hv * dv * 2 * 2 + Hv * 8)
+    roof = dict(bound="hbm", achieved=nbytes / (t_mean * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                traffic=measured_traffic("gdn_decode_kernel<128,true>", "decode"),
+                kernel="gdn_decode_kernel<128,true>", algorithmic_bytes=nbytes, avg_launch_us=t_mean * 1e3,
+                median_launch_us=t_med * 1e3, min_launch_us=t_min * 1e3)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    config = dict(workload="decode", sequences=B, Hqk=Hqk, Hv=Hv, dk=dk, dv=dv)
+    _line(args, B * Hv / (ms * 1e-3), ms, config, roof,
+          {"note": "value: one token per (sequence, value head) per step, state read and written in place"})
+
+
+def run_full_prefix(args):
+    """The group workload at r = 1, and the 5% tail replay of the same groups for the ratio."""
+    import torch
+    from linear_attention_state_amd import GroupReplay, tail_seqlens
+    w = build_workload("full_prefix", args.seed)
+    step, _ = make_step(w)
+    ms, host_ms, _ = time_steps(step, args.steps, args.warmup, False)
+    spec, gi = w["spec"], w["inputs"]
+    k = int(tail_seqlens([spec["m"]], 5, 100)[0][1])
+    h_tail = gi.h_tail[:, spec["m"] - k:].contiguous()
+    runner = GroupReplay(gi.weights, k, spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+    states = torch.empty((spec["G"], spec["L"], spec["Hv"], spec["dv"], spec["dk"]), dtype=torch.float32,
+                         device="cuda")
+    ms_tail, _, _ = time_steps(lambda: runner(h_tail, states_out=states), args.steps, args.warmup, False)
+    roof = group_roofline(w, args)
+    G, L, n = spec["G"], spec["L"], w["n"]
+    config = dict(workload="full_prefix", groups=G, layers_per_group=L, tokens_per_group=n, d_model=spec["d_model"],
+                  Hqk=spec["Hqk"], Hv=spec["Hv"], dk=spec["dk"], dv=spec["dv"], r="1", chunk=64)
+    _line(args, G * L * n * spec["Hv"] / (ms * 1e-3), ms, config, roof,
+          {"replay_5pct_ms_per_step": ms_tail, "full_over_replay": ms / ms_tail,
+           "note": "LA share of a full prefill of the 32768-token prefix versus its 5% tail replay"})
+
+
+def run_overlap(args):
+    """Host-to-device copy of the matched prefix's full-attention KV (pinned host memory, second
+    stream) beside the group replay: serial, overlapped, and the max(T_kv, T_replay) model."""
+    import torch
+    import synthetic
+    spec = synthetic.WORKLOADS["overlap"]
+    w = build_workload("group", args.seed)
+    step, _ = make_step(w)
+    kv_bytes = spec["kv_layers"] * 2 * spec["m"] * spec["kv_heads"] * spec["kv_head_dim"] * 2
+    host = torch.empty(kv_bytes, dtype=torch.uint8, pin_memory=True)
+    host.fill_(1)
+    dev = torch.empty(kv_bytes, dtype=torch.uint8, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()                        # default priority
+
+    def copy(stream):
+        with torch.cuda.stream(stream):
+            dev.copy_(host, non_blocking=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            fn()
+            e1.record(main)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return float(np.mean(out))
+
+    def overlapped():
+        side.wait_stream(main)
+        copy(side)
+        step()
+        main.wait_stream(side)
+
+    reps = max(3, min(args.steps, 10))
+    t_kv = timed(lambda: copy(main), reps)
+    t_rep = timed(step, reps)
+    t_serial = timed(lambda: (copy(main), step()), reps)
+    t_ovl = timed(overlapped, reps)
+    G, L, n, Hv = spec["G"], spec["L"], w["n"], spec["Hv"]
+    config = dict(workload="overlap", groups=G, layers_per_group=L, tokens_per_group=n, Hv=Hv,
+                  kv_bytes=kv_bytes, kv_layers=spec["kv_layers"], kv_heads=spec["kv_heads"],
+                  kv_head_dim=spec["kv_head_dim"], prefix_tokens=spec["m"])
+    roof = dict(bound="pcie", achieved=kv_bytes / (t_kv * 1e-3) / 1e9, peak=None, unit="GB/s", frac=None,
+                traffic=None, kernel="host-to-device copy of the prefix KV")
+    _line(args, G * L * n * Hv / (t_ovl * 1e-3), t_ovl, config, roof,
+          {"overlap": dict(t_kv_ms=t_kv, t_replay_ms=t_rep, t_serial_ms=t_serial, t_overlap_ms=t_ovl,
+                           model_max_ms=max(t_kv, t_rep), saved_vs_serial=1 - t_ovl / t_serial),
+           "note": "value: replayed token-heads/s with the KV copy running beside the replay"})
 
 
 # ---------------------------------------------------------------- main
@@ -309,6 +487,11 @@ def main():
         return
     import linear_attention_state_amd as tr
     tr.lib()   # fails loudly if the HIP library is not built
+    special = {"fidelity": run_fidelity, "decode": run_decode, "full_prefix": run_full_prefix,
+               "overlap": run_overlap}
+    if args.workload in special:
+        special[args.workload](args)
+        return
 
     w = build_workload(args.workload, args.seed)
     step, outs = make_step(w)

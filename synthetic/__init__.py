@@ -145,4 +145,17 @@ WORKLOADS = {
                   G=12, L=3, d_model=2048, Hqk=16, Hv=32, dk=128, dv=128, m=32768, r=(5, 100)),
     "varlen": dict(desc="64 hits, m ~ U{4096..131072}, r=0.05, 16 heads, dk=dv=128, bf16",
                    n_hits=64, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", r=(5, 100)),
+    "fidelity": dict(desc="one 32768-token sequence from zero, 16 heads, dk=dv=128, bf16; tails at "
+                          "r=0.05 and 0.10 of the same sequence",
+                     B=1, Hqk=16, Hv=16, dk=128, dv=128, dtype="bf16", m=32768, r=(5, 100),
+                     rs=[(5, 100), (10, 100)]),
+    "full_prefix": dict(desc="the group workload at r=1: 12 groups x 3 LA layers over all 32768 tokens",
+                        G=12, L=3, d_model=2048, Hqk=16, Hv=32, dk=128, dv=128, m=32768, r=(100, 100)),
+    "decode": dict(desc="one-token step on 36 instances x 32 v-heads (16 qk-heads), dk=dv=128, bf16 "
+                        "inputs, fp32 resident states",
+                   B=36, Hqk=16, Hv=32, dk=128, dv=128, dtype="bf16", m=32768, r=(5, 100)),
+    "overlap": dict(desc="the group workload (r=0.05) replayed while the matched prefix's full-attention "
+                         "KV is copied host to device on a second stream; KV widths are parameters",
+                    G=12, L=3, d_model=2048, Hqk=16, Hv=32, dk=128, dv=128, m=32768, r=(5, 100),
+                    kv_layers=12, kv_heads=2, kv_head_dim=256),
 }
