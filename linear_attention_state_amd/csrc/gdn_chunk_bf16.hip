@@ -172,7 +172,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int DK, int DV>
+// WITH_O: per-token outputs are produced (Q is loaded, Q K^T and P formed, O stored); without
+// them the kernel is the state-only scan.
+template <int DK, int DV, bool WITH_O>
 __global__ void __launch_bounds__(DV * 2, 2)
 gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
@@ -230,7 +232,8 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(beta + (size_t)bos * Hv + hv, (uint32_t)len * gb_stride);
     // outputs: stores past the sequence end fall outside the resource and are dropped
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o ? o + ((size_t)bos * Hv + hv) * DV : nullptr, o ? (uint32_t)len * v_stride : 0u);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(WITH_O ? o + ((size_t)bos * Hv + hv) * DV : nullptr,
+                                                WITH_O ? (uint32_t)len * v_stride : 0u);
 
     // ---- state: S^T tiles, tile r covers dk rows [32r, 32r+32), columns = own dv cols
     f32x16 St[KT_TILES];
@@ -312,7 +315,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         // This chunk's Q and V are issued after the tables: the gate values reloaded above
         // must not queue behind them.
-        {
+        if (WITH_O) {
             const uint32_t voff = (uint32_t)kq_row * kq_stride + (uint32_t)kq_col * 2;
 #pragma unroll
             for (int p = 0; p < NPASS; ++p) {
@@ -363,9 +366,11 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 *reinterpret_cast<f32x4*>(&sm.lw.LT[ci][r0]) = lv;
             }
         }
+        if (WITH_O) {
 #pragma unroll
-        for (int p = 0; p < NPASS; ++p)
-            *reinterpret_cast<bf16x8*>(&sm.Q[kq_row + RPP * p][kq_col]) = pq[p];
+            for (int p = 0; p < NPASS; ++p)
+                *reinterpret_cast<bf16x8*>(&sm.Q[kq_row + RPP * p][kq_col]) = pq[p];
+        }
         lds_barrier();
 
         // -------------------- P2: A = (I + L)^{-1} on wave 0; Q K^T on the other waves
@@ -461,7 +466,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             a30 = mma16(opL(3, 1), b10, a30);
             a30 = mma16(opL(3, 2), b20, a30);
             emit(3, 0, to_bf4(a30, -1.f));
-        } else {
+        } else if (WITH_O) {
             // Q K^T lower 16x16 tiles, kept in registers until P4
 #pragma unroll
             for (int it = 0; it < QK_PER_WAVE; ++it) {
@@ -529,7 +534,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         lds_barrier();
 
         // ------------------------------------------------------------ P4: P to LDS
-        if (o && wave > 0) {
+        if (WITH_O && wave > 0) {
 #pragma unroll
             for (int it = 0; it < QK_PER_WAVE; ++it) {
                 const int tt = (wave - 1) + (NW - 1) * it;
@@ -550,7 +555,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 }
             }
         }
-        if (wave == 0) {
+        if (WITH_O && wave == 0) {
             // the zero blocks above the diagonal inside each 32-row band (also zero for A - I)
 #pragma unroll
             for (int band = 0; band < 2; ++band)
@@ -565,89 +570,86 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         lds_barrier();
 
         // ------------------------------------------------ P5: state-dependent part
-        // Register budget: the state (64), U' (32) and the two 32-row output tiles (32) are
-        // the large live sets; state operands are converted once per k-step.
-        {
-            // U' = U0 + (-W) S^T and, with outputs, Y = Q S^T: one conversion of each state
-            // operand feeds up to four independent accumulators.
-            f32x16 Y[2];
-            if (o) {
-                Y[0] = zero16();
-                Y[1] = zero16();
+        // U' = U0 + (-W) S^T and, with outputs, Y = Q S^T: one conversion of each state operand
+        // feeds up to four independent accumulators.
+        f32x16 Y[2];
+        if (WITH_O) {
+            Y[0] = zero16();
+            Y[1] = zero16();
+        }
 #pragma unroll
-                for (int s = 0; s < KSTEPS_D; ++s) {
-                    const bf16x8 sb = acc_to_b(St[s >> 1], s);
+        for (int s = 0; s < KSTEPS_D; ++s) {
+            const bf16x8 sb = acc_to_b(St[s >> 1], s);
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) {
-                        U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
-                        Y[rt] = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), sb, Y[rt]);
-                    }
-                }
-                // O = diag(q_scale e^gamma) Y + P U'
-                const uint32_t ooff = (uint32_t)(4 * h2) * v_stride + (uint32_t)(col0 + l32) * 2;
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    f32x16 acc = Y[rt];
-#pragma unroll
-                    for (int j4 = 0; j4 < 4; ++j4) {
-                        const f32x4 e = tab4(sm.qeg, 32 * rt + 8 * j4 + 4 * h2);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[4 * j4 + i] *= e[i];
-                    }
-#pragma unroll
-                    for (int s = 0; s < 2 * rt + 2; ++s) {
-                        bf16x8 uh, ul;
-                        acc_to_b_split(U[s >> 1], s, uh, ul);
-                        const bf16x8 ph = kperm(&sm.np.p.Ph[32 * rt + l32][0], s, h2);
-                        const bf16x8 pl = kperm(&sm.np.p.Pl[32 * rt + l32][0], s, h2);
-                        acc = mma32(ph, uh, acc);
-                        acc = mma32(ph, ul, acc);
-                        acc = mma32(pl, uh, acc);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
-                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)acc[j]), ro, ooff, soff, 0);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < KSTEPS_D; ++s) {
-                    const bf16x8 sb = acc_to_b(St[s >> 1], s);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-                        U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
-                }
+            for (int rt = 0; rt < 2; ++rt) {
+                U[rt] = mma32(kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2), sb, U[rt]);
+                if (WITH_O) Y[rt] = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), sb, Y[rt]);
             }
-
-            // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K
+        }
+        // U' as the B operand of P U' (hi/lo split), before the decay scaling below
+        bf16x8 uh[4], ul[4];
+        if (WITH_O) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, uh[s], ul[s]);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
-                    const f32x4 d = tab4(sm.dec, 32 * rt + 8 * j4 + 4 * h2);
+                    const f32x4 e = tab4(sm.qeg, 32 * rt + 8 * j4 + 4 * h2);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) U[rt][4 * j4 + i] *= d[i];
+                    for (int i = 0; i < 4; ++i) Y[rt][4 * j4 + i] *= e[i];
                 }
-            bf16x8 dh[4], dl[4];
+        }
+        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K, and with outputs
+        // O = diag(q_scale e^gamma) Y + P U' in the same token k-steps: the two products use
+        // independent accumulators, so their MFMAs interleave.
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, dh[s], dl[s]);
-            const float decay = sm.eg[CH - 1];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int r = 0; r < KT_TILES; ++r)
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 d = tab4(sm.dec, 32 * rt + 8 * j4 + 4 * h2);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) St[r][j] *= decay;
-            // k-step outer, tile inner: consecutive MFMAs hit independent accumulators
+                for (int i = 0; i < 4; ++i) U[rt][4 * j4 + i] *= d[i];
+            }
+        const float decay = sm.eg[CH - 1];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int r = 0; r < KT_TILES; ++r)
 #pragma unroll
-                for (int r = 0; r < KT_TILES; ++r) {
-                    const bf16x8 a = cat(lds_tr4(&sm.K[16 * s + 4 * h2 + tr_p][32 * r + tr_c]),
-                                         lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * r + tr_c]));
-                    St[r] = mma32(a, dh[s], St[r]);
-                    St[r] = mma32(a, dl[s], St[r]);
+            for (int j = 0; j < 16; ++j) St[r][j] *= decay;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 dh, dl;
+            acc_to_b_split(U[s >> 1], s, dh, dl);
+#pragma unroll
+            for (int r = 0; r < KT_TILES; ++r) {
+                const bf16x8 a = cat(lds_tr4(&sm.K[16 * s + 4 * h2 + tr_p][32 * r + tr_c]),
+                                     lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * r + tr_c]));
+                St[r] = mma32(a, dh, St[r]);
+                St[r] = mma32(a, dl, St[r]);
+            }
+            if (WITH_O) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    if (s < 2 * rt + 2) {                  // P is lower triangular
+                        const bf16x8 ph = kperm(&sm.np.p.Ph[32 * rt + l32][0], s, h2);
+                        const bf16x8 pl = kperm(&sm.np.p.Pl[32 * rt + l32][0], s, h2);
+                        Y[rt] = mma32(ph, uh[s], Y[rt]);
+                        Y[rt] = mma32(ph, ul[s], Y[rt]);
+                        Y[rt] = mma32(pl, uh[s], Y[rt]);
+                    }
                 }
             }
+        }
+        if (WITH_O) {
+            const uint32_t ooff = (uint32_t)(4 * h2) * v_stride + (uint32_t)(col0 + l32) * 2;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)Y[rt][j]), ro,
+                                                          ooff, soff, 0);
+                }
         }
         lds_barrier();
     }
@@ -665,9 +667,9 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 }
 
-template <int DK, int DV>
-hipError_t launch(const GdnArgs& a, hipStream_t stream) {
-    auto kern = gdn_chunk_bf16_kernel<DK, DV>;
+template <int DK, int DV, bool WITH_O>
+hipError_t launch_variant(const GdnArgs& a, hipStream_t stream) {
+    auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O>;
     const size_t smem = sizeof(Smem<DK, DV>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
@@ -678,6 +680,11 @@ hipError_t launch(const GdnArgs& a, hipStream_t stream) {
                        a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
                        a.state_in, a.state_identity, a.state_out, (bf16*)a.o);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch(const GdnArgs& a, hipStream_t stream) {
+    return a.o ? launch_variant<DK, DV, true>(a, stream) : launch_variant<DK, DV, false>(a, stream);
 }
 
 }  // namespace
