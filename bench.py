@@ -62,10 +62,16 @@ def parse():
 
 
 # ---------------------------------------------------------------- HBM traffic
-def _sha256(path):
+def kernel_digest(path):
+    """sha256 of a kernel source with its // comments and blank lines removed: edits to the
+    comments do not change the kernel the counts were taken on."""
     import hashlib
-    with open(os.path.join(HERE, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(os.path.join(HERE, path), encoding="utf-8") as f:
+        text = f.read()
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.split("\n")]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()
 
 
 def measured_traffic(kernel_name, workload):
@@ -83,7 +89,7 @@ def measured_traffic(kernel_name, workload):
     if not ent:
         return None
     src = KERNEL_SOURCES.get(key.split("<")[0].split("@")[0])
-    if src is None or ent.get("source_sha256") != _sha256(src):
+    if src is None or ent.get("source_digest") != kernel_digest(src):
         return None
     return ent.get("hbm_bytes_per_launch")
 

@@ -26,14 +26,20 @@
 // barriers and latencies hide behind the other's MFMA work.  Wave w owns value columns
 // [32w, 32w + 32) of the state, kept in MFMA accumulator registers as S^T tiles (dk rows
 // x 32 dv columns).  Per chunk:
-//   P0  stage K, Q (row-major) in LDS; gate cumsum; prefetch the next chunk's K, Q, g, beta
-//   P1  K K^T and Q K^T, lower 16x16 tiles on 16x16x32 MFMA; L to LDS, Q K^T kept in registers
-//   P2  A = (I + L)^{-1} on one wave: fp32 forward substitution of the four 16x16 diagonal
-//       blocks (a 16-lane group per block), 16x16x16 MFMA merges held in registers
+//   P0  stage K (loaded one chunk ahead, with g and beta); gate cumsum and the exp2 tables;
+//       issue this chunk's Q and V loads and the next chunk's K, g, beta loads
+//   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L^T (fp32) in LDS;
+//       stage Q
+//   P2  A = (I + L)^{-1} on wave 0: fp32 back substitution of the four 16x16 diagonal blocks
+//       (a 16-lane group per block, each lane one row), 16x16x16 MFMA merges in registers;
+//       the other waves form the Q K^T tiles (registers)
 //   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
 //       K^T operands come from the row-major K tile through LDS transpose reads
 //   P4  P (bf16 hi/lo) to LDS, over the dead (A - I) tiles
-//   P5  U' = U0 + (-W) S^T ;  O = e^gamma q_scale Q S^T + P U' ;  S update
+//   P5  U' = U0 + (-W) S^T and Y = Q S^T in one pass over the state operands; then the state
+//       update S <- e^{gamma_n} S + U'^T D K and O = e^gamma q_scale Y + P U' share the
+//       token k-steps (independent accumulators); O stored
+// The state-only variant (WITH_O = false) drops Q, Q K^T, P and O.
 // An accumulator feeds the next product directly as its B operand: the contraction index
 // is permuted the same way on both operands (see kperm()).
 #include "internal.h"
