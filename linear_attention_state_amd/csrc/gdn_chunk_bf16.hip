@@ -67,6 +67,16 @@ __device__ __forceinline__ f32x4 mma16k32(const bf16x8& a, const bf16x8& b, cons
 __device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// fp32 16x16 product on 16x16x4 fp32 MFMA.  X in row layout (lane (m, g = l / 16) holds
+// X[m][4g .. 4g+3]) times Y in accumulator layout (lane (n, g) holds Y[4g .. 4g+3][n]),
+// plus C, gives the accumulator layout; step s pairs contraction index 4g + s on both sides.
+// With the operands swapped (Y's registers as X, X's as Y) the same call gives the product
+// transposed, i.e. in row layout.
+__device__ __forceinline__ f32x4 mm16f(const f32x4& xrow, const f32x4& yacc, f32x4 c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[s], yacc[s], c, 0, 0, 0);
+    return c;
+}
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -154,7 +164,10 @@ struct Smem {
     bf16 K[CH][DK + 16];        // key rows (padding keeps the transpose reads conflict-free)
     bf16 Q[CH][DK + 8];         // query rows
     union {
-        float LT[CH][RS_L];     // L transposed (LT[i][t] = L_ti, i < t), fp32: P1 .. P2
+        struct {
+            float Ld[4][16][20];    // diagonal 16x16 blocks of L, transposed (Ld[b][i][t] = L_ti), fp32
+            bf16 Lb[CH][RS_T];      // L row-major in bf16 (off-diagonal blocks used): P1 .. P2
+        } l;
         bf16 Wn[CH][DK + 8];    // -W rows: P3 .. P5
     } lw;
     union {
@@ -162,6 +175,7 @@ struct Smem {
         struct { bf16 Ph[CH][RS_T]; bf16 Pl[CH][RS_T]; } p;    // P hi / lo: P4 .. P5
     } np;
     bf16 Ad[4][16][24];         // diagonal 16x16 blocks of A (bf16 merge operands)
+    bf16 AdT[4][16][24];        // the same blocks transposed
     // per-token tables of the chunk (padded tokens: g = beta = 0)
     float g2[CH];               // gamma_t * log2(e)
     float bt[CH];               // beta_t
@@ -196,7 +210,10 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     constexpr int RPP = NT / TPR;          // rows per pass
     constexpr int NPASS = CH / RPP;
     constexpr int G_PER_WAVE = (10 + NW - 1) / NW;          // K K^T tiles per wave (P1)
-    constexpr int QK_PER_WAVE = (10 + NW - 2) / (NW - 1);   // Q K^T tiles per wave 1.. (P2)
+    // Q K^T tiles (P2): wave w takes tiles [qk_begin(w), qk_begin(w + 1)); the waves with the
+    // longer inverse merge chains (low w) take fewer.
+    constexpr int QK_PER_WAVE = NW == 4 ? 4 : 6;
+    auto qk_begin = [](int w) { return NW == 4 ? w * (w + 1) / 2 : (w == 0 ? 0 : (w == 1 ? 4 : 10)); };
     constexpr float LOG2E = 1.4426950408889634f;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -354,22 +371,38 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             if (tt < 10) {
                 const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
                 const int cb = tt - rb * (rb + 1) / 2;
-                const bf16* xrow = &sm.K[16 * rb + l16][0];
-                const bf16* krow = &sm.K[16 * cb + l16][0];
+                // Diagonal tiles come out with lane (n, q) holding rows 4q..4q+3 of column n (the
+                // layout the inverse reads as fp32); off-diagonal tiles are formed transposed
+                // (operands swapped), so lane (m, q) holds row m, columns 4q..4q+3, stored as bf16
+                // rows for the merges' A operands.
+                const bool diag = rb == cb;
+                const bf16* xrow = &sm.K[16 * (diag ? rb : cb) + l16][0];
+                const bf16* krow = &sm.K[16 * (diag ? cb : rb) + l16][0];
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int s = 0; s < DK / 32; ++s)
                     acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
                                    *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
-                const int ci = 16 * cb + l16;
-                const float gi = sm.g2[ci];
-                const int r0 = 16 * rb + 4 * g4;
-                const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
-                f32x4 lv;
+                if (diag) {
+                    const int ci = 16 * cb + l16;
+                    const float gi = sm.g2[ci];
+                    const int r0 = 16 * rb + 4 * g4;
+                    const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
+                    f32x4 lv;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
-                *reinterpret_cast<f32x4*>(&sm.lw.LT[ci][r0]) = lv;
+                    for (int j = 0; j < 4; ++j)
+                        lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
+                    *reinterpret_cast<f32x4*>(&sm.lw.l.Ld[rb][l16][4 * g4]) = lv;
+                } else {
+                    const int t = 16 * rb + l16;                  // row (later token)
+                    const int c0 = 16 * cb + 4 * g4;              // columns c0..c0+3 (earlier tokens)
+                    const float gt = sm.g2[t], bt = sm.bt[t];
+                    const f32x4 gi = tab4(sm.g2, c0);
+                    bf16x4 lv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) lv[j] = (bf16)(bt * __builtin_amdgcn_exp2f(gt - gi[j]) * acc[j]);
+                    *reinterpret_cast<bf16x4*>(&sm.lw.l.Lb[t][c0]) = lv;
+                }
             }
         }
         if (WITH_O) {
@@ -379,64 +412,56 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         lds_barrier();
 
-        // -------------------- P2: A = (I + L)^{-1} on wave 0; Q K^T on the other waves
-        f32x4 tacc[QK_PER_WAVE];
-        if (wave == 0) {
-            // Diagonal blocks D_b = (I + L_bb)^{-1}: the 16-lane group g4 takes block g4 and lane
-            // j solves (I + L_bb^T) y = e_j by back substitution, so y is row j of D_b and the
-            // block leaves the lane as whole rows.
-            {
-                const int base = 16 * g4;
-                const int j = l16;
-                float y[16];
+        // ------------------- P2: A = (I + L)^{-1}, two steps; Q K^T tiles on every wave
+        // Step 1: the diagonal blocks D_b = (I + L_bb)^{-1}, block b on wave b % NW, in fp32 on
+        // MFMA: L_bb is strictly lower triangular (nilpotent), so
+        //     D_b = (I - L)(I + L^2)(I + L^4)(I + L^8).
+        for (int b = wave; b < 4; b += NW) {
+            const int base = 16 * b;
+            f32x4 Lr, La;                                   // L_bb in row and accumulator layout
 #pragma unroll
-                for (int i = 15; i >= 0; --i) {
-                    float acc = (i == j) ? 1.f : 0.f;
+            for (int e = 0; e < 4; ++e) Lr[e] = sm.lw.l.Ld[b][4 * g4 + e][l16];
+            La = *reinterpret_cast<const f32x4*>(&sm.lw.l.Ld[b][l16][4 * g4]);
+            const f32x4 L2a = mm16f(Lr, La, zero4()), L2r = mm16f(La, Lr, zero4());
+            const f32x4 L4a = mm16f(L2r, L2a, zero4()), L4r = mm16f(L2a, L2r, zero4());
+            const f32x4 L8r = mm16f(L4a, L4r, zero4());
+            f32x4 D;                                        // I - L, accumulator layout
 #pragma unroll
-                    for (int kk = i + 1; kk < 16; ++kk) acc -= sm.lw.LT[base + i][base + kk] * y[kk];
-                    y[i] = acc;
-                }
-                bf16x8 ad0, ad1, nb0, nb1, ng0, ng1;
+            for (int j = 0; j < 4; ++j) D[j] = (4 * g4 + j == l16 ? 1.f : 0.f) - La[j];
+            D = mm16f(L2r, D, D);
+            D = mm16f(L4r, D, D);
+            D = mm16f(L8r, D, D);                           // lane (n, g): D[4g + j][n]
+            const float bn = sm.bt[base + l16], bgn = sm.bg[base + l16];
+            bf16x4 ad;
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 bt = tab4(sm.bt, base + 4 * i4), bg = tab4(sm.bg, base + 4 * i4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * i4 + e;
-                        const float nn = (i < j) ? y[i] : 0.f;
-                        bf16x8& ad = i < 8 ? ad0 : ad1;
-                        bf16x8& nb = i < 8 ? nb0 : nb1;
-                        bf16x8& ng = i < 8 ? ng0 : ng1;
-                        ad[i & 7] = (bf16)y[i];
-                        nb[i & 7] = (bf16)(nn * bt[e]);
-                        ng[i & 7] = (bf16)(nn * bg[e]);
-                    }
-                }
-                *reinterpret_cast<bf16x8*>(&sm.Ad[g4][j][0]) = ad0;
-                *reinterpret_cast<bf16x8*>(&sm.Ad[g4][j][8]) = ad1;
-                *reinterpret_cast<bf16x8*>(&sm.np.n.Nb[base + j][base]) = nb0;
-                *reinterpret_cast<bf16x8*>(&sm.np.n.Nb[base + j][base + 8]) = nb1;
-                *reinterpret_cast<bf16x8*>(&sm.np.n.Nbg[base + j][base]) = ng0;
-                *reinterpret_cast<bf16x8*>(&sm.np.n.Nbg[base + j][base + 8]) = ng1;
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                ad[j] = (bf16)D[j];
+                const float nn = r > l16 ? D[j] : 0.f;      // strictly lower part: A - I
+                sm.np.n.Nb[base + r][base + l16] = (bf16)(nn * bn);
+                sm.np.n.Nbg[base + r][base + l16] = (bf16)(nn * bgn);
             }
-            // merges: A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj, 16x16x16 MFMA.  16x16x16 layouts:
-            // A operand lane (m = l % 16, q = l / 16) holds row m, k = 4q..4q+3; B operand and
-            // accumulator hold rows 4q..4q+3 of column l % 16, so a result feeds the next
-            // product's B operand as it stands.
-            auto opL = [&](int i, int kb) {          // A operand: L block (i, kb), from L^T
-                bf16x4 r;
+            *reinterpret_cast<bf16x4*>(&sm.AdT[b][l16][4 * g4]) = ad;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = (bf16)sm.lw.LT[16 * kb + 4 * g4 + e][16 * i + l16];
-                return r;
+            for (int j = 0; j < 4; ++j) sm.Ad[b][4 * g4 + j][l16] = ad[j];
+        }
+        lds_barrier();
+
+        // Step 2: off-diagonal blocks, one block column per wave:
+        // A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj on 16x16x16 bf16 MFMA.  16x16x16 layouts: the A
+        // operand lane (m = l % 16, q = l / 16) holds row m, k = 4q..4q+3; the B operand and the
+        // accumulator hold rows 4q..4q+3 of column l % 16, so a result feeds the next product's
+        // B operand as it stands.
+        f32x4 tacc[QK_PER_WAVE];
+        {
+            auto opL = [&](int i, int kb) {          // A operand: L block (i, kb)
+                return *reinterpret_cast<const bf16x4*>(&sm.lw.l.Lb[16 * i + l16][16 * kb + 4 * g4]);
             };
-            auto opAd = [&](int i) {                 // A operand: diagonal block A_ii
+            auto opAd = [&](int i) {                 // A operand: diagonal block A_ii (row layout)
                 return *reinterpret_cast<const bf16x4*>(&sm.Ad[i][l16][4 * g4]);
             };
             auto opBd = [&](int kb) {                // B operand: diagonal block A_kk
-                bf16x4 r;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = sm.Ad[kb][4 * g4 + e][l16];
-                return r;
+                return *reinterpret_cast<const bf16x4*>(&sm.AdT[kb][l16][4 * g4]);
             };
             // Block (i, j) of A - I is -(A_ii T); its transpose -(T^T A_ii^T) comes out of the MFMA
             // in row order (lane (n, q) holds row n, columns 4q..4q+3), so it is written as
@@ -455,39 +480,41 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 *reinterpret_cast<bf16x4*>(&sm.np.n.Nb[16 * i + l16][c0]) = nb;
                 *reinterpret_cast<bf16x4*>(&sm.np.n.Nbg[16 * i + l16][c0]) = ng;
             };
-            // distance 1
-            const bf16x4 t10 = to_bf4(mma16(opL(1, 0), opBd(0), zero4()), -1.f);
-            const bf16x4 t21 = to_bf4(mma16(opL(2, 1), opBd(1), zero4()), -1.f);
-            const bf16x4 t32 = to_bf4(mma16(opL(3, 2), opBd(2), zero4()), -1.f);
-            const bf16x4 b10 = to_bf4(mma16(opAd(1), t10, zero4()), 1.f);
-            const bf16x4 b21 = to_bf4(mma16(opAd(2), t21, zero4()), 1.f);
-            emit(1, 0, t10); emit(2, 1, t21); emit(3, 2, t32);
-            // distance 2
-            const bf16x4 t20 = to_bf4(mma16(opL(2, 1), b10, mma16(opL(2, 0), opBd(0), zero4())), -1.f);
-            const bf16x4 t31 = to_bf4(mma16(opL(3, 2), b21, mma16(opL(3, 1), opBd(1), zero4())), -1.f);
-            const bf16x4 b20 = to_bf4(mma16(opAd(2), t20, zero4()), 1.f);
-            emit(2, 0, t20); emit(3, 1, t31);
-            // distance 3
-            f32x4 a30 = mma16(opL(3, 0), opBd(0), zero4());
-            a30 = mma16(opL(3, 1), b10, a30);
-            a30 = mma16(opL(3, 2), b20, a30);
-            emit(3, 0, to_bf4(a30, -1.f));
-        } else if (WITH_O) {
-            // Q K^T lower 16x16 tiles, kept in registers until P4
+            for (int j = wave; j < 3; j += NW) {
+                const bf16x4 dj = opBd(j);
+                bf16x4 a1, a2;                        // A_{j+1,j}, A_{j+2,j} as B operands
+                const bf16x4 t1 = to_bf4(mma16(opL(j + 1, j), dj, zero4()), -1.f);
+                if (j + 1 < 3) a1 = to_bf4(mma16(opAd(j + 1), t1, zero4()), 1.f);
+                emit(j + 1, j, t1);
+                if (j + 2 <= 3) {
+                    const bf16x4 t2 = to_bf4(mma16(opL(j + 2, j + 1), a1, mma16(opL(j + 2, j), dj, zero4())), -1.f);
+                    if (j + 2 < 3) a2 = to_bf4(mma16(opAd(j + 2), t2, zero4()), 1.f);
+                    emit(j + 2, j, t2);
+                }
+                if (j + 3 <= 3) {
+                    f32x4 acc = mma16(opL(3, 0), dj, zero4());
+                    acc = mma16(opL(3, 1), a1, acc);
+                    acc = mma16(opL(3, 2), a2, acc);
+                    emit(3, 0, to_bf4(acc, -1.f));
+                }
+            }
+            if (WITH_O) {
+                // Q K^T lower 16x16 tiles, kept in registers until P4
 #pragma unroll
-            for (int it = 0; it < QK_PER_WAVE; ++it) {
-                const int tt = (wave - 1) + (NW - 1) * it;
-                if (tt < 10) {
-                    const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-                    const int cb = tt - rb * (rb + 1) / 2;
-                    const bf16* xrow = &sm.Q[16 * rb + l16][0];
-                    const bf16* krow = &sm.K[16 * cb + l16][0];
-                    f32x4 acc = zero4();
+                for (int it = 0; it < QK_PER_WAVE; ++it) {
+                    const int tt = qk_begin(wave) + it;
+                    if (tt < qk_begin(wave + 1)) {
+                        const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                        const int cb = tt - rb * (rb + 1) / 2;
+                        const bf16* xrow = &sm.Q[16 * rb + l16][0];
+                        const bf16* krow = &sm.K[16 * cb + l16][0];
+                        f32x4 acc = zero4();
 #pragma unroll
-                    for (int s = 0; s < DK / 32; ++s)
-                        acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
-                                       *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
-                    tacc[it] = acc;
+                        for (int s = 0; s < DK / 32; ++s)
+                            acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
+                                           *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
+                        tacc[it] = acc;
+                    }
                 }
             }
         }
@@ -540,11 +567,11 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         lds_barrier();
 
         // ------------------------------------------------------------ P4: P to LDS
-        if (WITH_O && wave > 0) {
+        if (WITH_O) {
 #pragma unroll
             for (int it = 0; it < QK_PER_WAVE; ++it) {
-                const int tt = (wave - 1) + (NW - 1) * it;
-                if (tt < 10) {
+                const int tt = qk_begin(wave) + it;
+                if (tt < qk_begin(wave + 1)) {
                     const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
                     const int cb = tt - rb * (rb + 1) / 2;
                     const int ci = 16 * cb + l16;
