@@ -17,6 +17,7 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -70,12 +71,17 @@ constexpr int WAVES_N = 4, TM = 4, TN = 2;            // wave grid 2 x 4, wave t
 constexpr int NTHREADS = 512;
 constexpr int ROW_BYTES = BK * 2;                    // 128
 constexpr int SLOT_BYTES = (BM + BN) * ROW_BYTES;    // A rows then B rows: 64 KB
-constexpr int SMEM_BYTES = 2 * SLOT_BYTES;           // 128 KB
+constexpr int RING_BYTES = 2 * SLOT_BYTES;           // 128 KB
+// Epilogue staging, one private region per wave (its 128 x 64 outputs): bf16 rows of 72 for
+// the layer-in outputs, or fp32 rows of 68 for the residual (64 tokens per pass).
+constexpr int STG_BF16_ROW = 64 + 8, STG_F32_ROW = 64 + 4;
+constexpr int STG_WAVE_BYTES = 128 * STG_BF16_ROW * 2;                 // 18 KB
+static_assert(64 * STG_F32_ROW * 4 <= STG_WAVE_BYTES, "fp32 half tile fits the wave's region");
+constexpr int SSBUF_OFFSET = 8 * STG_WAVE_BYTES;                       // row sums of squares
+constexpr int SMEM_BYTES = SSBUF_OFFSET + 8 * 4 * 32 * 4;              // 148 KB
+static_assert(SMEM_BYTES >= RING_BYTES, "the staging reuses the ring");
 constexpr int LOADS_PER_WAVE = SLOT_BYTES / 1024 / (NTHREADS / 64);   // 1 KB per load instruction
 constexpr int GROUP_M = 8;                           // row tiles per band of the tile order
-constexpr int EPI_ROWS = 64;                         // the epilogue stages a quarter tile at a time
-constexpr int STAGE_STRIDE = BN + 4;                 // fp32 elements per staged row
-static_assert(EPI_ROWS * STAGE_STRIDE * 4 <= SMEM_BYTES, "epilogue staging must fit in the ring");
 
 enum { EPI_LAYER_IN = 0, EPI_RESIDUAL = 1 };
 
@@ -171,7 +177,7 @@ gemm_tn_kernel(const GemmParams p)
         }
     }
     auto issue = [&](int kt) {
-        unsigned char* slot = smem + (kt & 1) * SLOT_BYTES + wave * LOADS_PER_WAVE * 1024;
+        unsigned char* slot = smem + (kt & 1) * SLOT_BYTES + wave * LOADS_PER_WAVE * 1024;   // ring: [0, RING_BYTES)
 #pragma unroll
         for (int j = 0; j < LOADS_PER_WAVE; ++j)
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_void*)(slot + 1024 * j), 16, 0, 0);
@@ -209,91 +215,137 @@ gemm_tn_kernel(const GemmParams p)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mma32(af[i], bfr[j], acc[i][j]);
+                // operands swapped: the accumulator holds the tile transposed, so each lane ends
+                // with one token and runs of 4 consecutive output columns
+                for (int j = 0; j < TN; ++j) acc[i][j] = mma32(bfr[j], af[i], acc[i][j]);
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- epilogue, one 64-row quarter at a time: the waves holding that quarter stage their
-    // fp32 values in LDS, then eight threads take each row (32 columns each); four threads
-    // cover one 128-column segment (one head).
-    float (*stage)[STAGE_STRIDE] = reinterpret_cast<float (*)[STAGE_STRIDE]>(smem);
-    const int er = tid >> 3;             // row within the quarter
-    const int eq = tid & 7;              // columns [32 eq, 32 eq + 32)
-    const float* srow = &stage[er][32 * eq];
-    const int seg = 2 * nt + (eq >> 2);  // 128-column segment of the output
-    // fully unrolled: the accumulator tiles must be indexed with constants to stay in registers
+    // ---- epilogue.  acc[i][j] element e of lane (l32, h2) is output row (token)
+    // 128 wm + 32 i + l32 and column 64 wn + 32 j + 8 (e / 4) + 4 h2 + e % 4.  Each wave turns
+    // its 128 x 64 block around in a private LDS region, then writes whole 128-byte row runs.
+    unsigned char* stg = smem + wave * STG_WAVE_BYTES;
+    const int rr = lane >> 3;                 // read-back: row within a group of 8, 16-byte chunk
+    const int rc = (lane & 7) * 8;            // first of 8 columns
+    if (EPI == EPI_RESIDUAL) {
+        float* st = reinterpret_cast<float*>(stg);
+        auto put = [&](const f32x16 (&a)[TN], int ii) {
 #pragma unroll
-    for (int qr = 0; qr < BM / EPI_ROWS; ++qr) {
-        if (wm == (qr >> 1)) {
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 x;
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                    for (int e = 0; e < 4; ++e) x[e] = a[j][4 * q4 + e];
+                    *reinterpret_cast<f32x4*>(st + (32 * ii + l32) * STG_F32_ROW + 32 * j + 8 * q4 + 4 * h2) = x;
+                }
+        };
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int r = 32 * ii + 8 * (e >> 2) + 4 * h2 + (e & 3);
-                        stage[r][wn * TN * 32 + 32 * j + l32] = acc[2 * (qr & 1) + ii][j][e];
+        for (int half = 0; half < 2; ++half) {
+            if (half == 0) { put(acc[0], 0); put(acc[1], 1); } else { put(acc[2], 0); put(acc[3], 1); }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int row = 8 * t + rr;                      // 0..63
+                const int m = mt * BM + wm * TM * 32 + 64 * half + row;
+                const int n0 = nt * BN + wn * TN * 32 + rc;
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + row * STG_F32_ROW + rc);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + row * STG_F32_ROW + rc + 4);
+                if (m < p.M && n0 < p.N) {
+                    const size_t off = ((size_t)g * p.M + m) * p.N + n0;
+                    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(p.x_in + off);
+                    bf16x8 ov;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ov[e] = (bf16)((float)xv[e] + v0[e]);
+                        ov[4 + e] = (bf16)((float)xv[4 + e] + v1[e]);
                     }
+                    *reinterpret_cast<bf16x8*>(p.x_out + off) = ov;
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half lands
         }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        return;
+    }
 
-        const int m = mt * BM + EPI_ROWS * qr + er;
-        const bool valid = m < p.M;
-        const size_t grow = (size_t)g * p.M + m;      // global token row
-        if (EPI == EPI_RESIDUAL) {
-            const int n0 = nt * BN + 32 * eq;
-            if (valid && n0 < p.N) {
-                const bf16* xi = p.x_in + grow * p.N + n0;
-                bf16* xo = p.x_out + grow * p.N + n0;
+    // EPI_LAYER_IN.  128-column segments: q heads, k heads, v heads, then one segment of gate
+    // logits ([0, Hv) z_a, [Hv, 2 Hv) z_b).  A segment spans waves wn and wn ^ 1; the row sums
+    // of squares for the q / k L2 norms meet through LDS.
+    float ss[TM];
 #pragma unroll
-                for (int c = 0; c < 32; c += 8) {
-                    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xi + c);
-                    bf16x8 ov;
+    for (int i = 0; i < TM; ++i) {
+        float t = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)((float)xv[e] + srow[c + e]);
-                    *reinterpret_cast<bf16x8*>(xo + c) = ov;
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) t = fmaf(acc[i][j][e], acc[i][j][e], t);
+        ss[i] = t + __shfl_xor(t, 32, 64);
+    }
+    float* ssbuf = reinterpret_cast<float*>(smem + SSBUF_OFFSET);      // [waves][TM][32]
+    if (h2 == 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) ssbuf[(wave * TM + i) * 32 + l32] = ss[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ss[i] += ssbuf[((wave ^ 1) * TM + i) * 32 + l32];
+
+    const int seg = 2 * nt + (wn >> 1);
+    const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
+    if (seg < nv) {
+        // q, k (L2-normalised rows, q also scaled) or v: bf16 through the wave's staging rows
+        const bool is_qk = seg < nk, is_q = seg < nq;
+        bf16* st = reinterpret_cast<bf16*>(stg);
+        auto put = [&](const f32x16 (&a)[TN], float ssi, int i) {
+            const float scale = is_qk ? (is_q ? p.q_scale : 1.f) / sqrtf(ssi + 1e-6f) : 1.f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)(a[j][4 * q4 + e] * scale);
+                    *reinterpret_cast<bf16x4*>(st + (32 * i + l32) * STG_BF16_ROW + 32 * j + 8 * q4 + 4 * h2) = ov;
                 }
-            }
-        } else {
-            // EPI_LAYER_IN: segments are the q heads, the k heads, the v heads, then one
-            // segment of gate logits ([0, Hv) z_a, [Hv, 2 Hv) z_b)
-            float ss = 0.f;
+        };
+        put(acc[0], ss[0], 0);
+        put(acc[1], ss[1], 1);
+        put(acc[2], ss[2], 2);
+        put(acc[3], ss[3], 3);
+        bf16* base = is_qk ? (is_q ? p.q : p.k) : p.v;
+        const int heads = is_qk ? p.Hqk : p.Hv;
+        const int head = is_qk ? (is_q ? seg : seg - nq) : seg - nk;
 #pragma unroll
-            for (int c = 0; c < 32; ++c) ss = fmaf(srow[c], srow[c], ss);
-            ss += __shfl_xor(ss, 1, 64);
-            ss += __shfl_xor(ss, 2, 64);
-            const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
-            if (valid && seg < nk) {
-                const bool is_q = seg < nq;
-                const float scale = (is_q ? p.q_scale : 1.f) / sqrtf(ss + 1e-6f);
-                const int head = is_q ? seg : seg - nq;
-                bf16* dst = (is_q ? p.q : p.k) + (grow * p.Hqk + head) * 128 + 32 * (eq & 3);
-#pragma unroll
-                for (int c = 0; c < 32; c += 8) {
-                    bf16x8 ov;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)(srow[c + e] * scale);
-                    *reinterpret_cast<bf16x8*>(dst + c) = ov;
-                }
-            } else if (valid && seg < nv) {
-                bf16* dst = p.v + (grow * p.Hv + (seg - nk)) * 128 + 32 * (eq & 3);
-#pragma unroll
-                for (int c = 0; c < 32; c += 8) {
-                    bf16x8 ov;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ov[e] = (bf16)srow[c + e];
-                    *reinterpret_cast<bf16x8*>(dst + c) = ov;
-                }
-            } else if (valid && seg == nv) {
-                for (int c = 0; c < 32; ++c) {
-                    const int cg = 32 * (eq & 3) + c;
-                    if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(srow[c]);
-                    else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(srow[c]);
-                }
-            }
+        for (int t = 0; t < 16; ++t) {
+            const int row = 8 * t + rr;                          // 0..127
+            const int m = mt * BM + wm * TM * 32 + row;
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(st + row * STG_BF16_ROW + rc);
+            if (m < p.M)
+                *reinterpret_cast<bf16x8*>(base + (((size_t)g * p.M + m) * heads + head) * 128 + (wn & 1) * 64 + rc) = x;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else if (seg == nv) {
+        // gate logits: few columns, written from registers
+        const int cseg = (wn & 1) * TN * 32 + 4 * h2;
+        auto gates = [&](const f32x16 (&a)[TN], int i) {
+            const int m = mt * BM + wm * TM * 32 + 32 * i + l32;
+            if (m >= p.M) return;
+            const size_t grow = (size_t)g * p.M + m;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int cg = cseg + 32 * j + 8 * q4 + e;
+                        const float z = a[j][4 * q4 + e];
+                        if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(z);
+                        else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(z);
+                    }
+        };
+        gates(acc[0], 0);
+        gates(acc[1], 1);
+        gates(acc[2], 2);
+        gates(acc[3], 3);
     }
 }
 
