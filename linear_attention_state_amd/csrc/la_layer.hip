@@ -121,10 +121,18 @@ __device__ __forceinline__ const bf16* row_src(const GemmParams& p, int g, int n
     return nullptr;
 }
 
-__device__ __forceinline__ float softplus_f(float z) { return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z))); }
+// Gates on the hardware exp2 / log2 (about 1 ulp each).  softplus(z) = max(z, 0) + log1p(t),
+// t = e^{-|z|} in (0, 1]; log1p(t) is taken as log(u) with u = 1 + t rounded, corrected to first
+// order for that rounding: log(1 + t) = log(u) - (u - 1 - t) / u + O(((u - 1 - t) / u)^2).
+__device__ __forceinline__ float softplus_f(float z) {
+    const float t = __expf(-fabsf(z));
+    const float u = 1.f + t;
+    return fmaxf(z, 0.f) + (__logf(u) - ((u - 1.f) - t) / u);
+}
 __device__ __forceinline__ float sigmoid_f(float z) {
-    const float e = expf(-fabsf(z));
-    return z >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+    const float t = __expf(-fabsf(z));
+    const float r = 1.f / (1.f + t);
+    return z >= 0.f ? r : t * r;
 }
 
 // Physical position of logical 16-byte chunk c in slot row r is c ^ chunk_swz(r).
@@ -333,14 +341,29 @@ gemm_tn_kernel(const GemmParams p)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int cg0 = cseg + 32 * j + 8 * q4;          // four consecutive columns
+                    if (cg0 >= 2 * p.Hv) continue;
+                    if ((p.Hv & 3) == 0) {                          // all four in g or all in beta
+                        const bool is_g = cg0 < p.Hv;
+                        f32x4 r;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int cg = cseg + 32 * j + 8 * q4 + e;
-                        const float z = a[j][4 * q4 + e];
-                        if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(z);
-                        else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(z);
+                        for (int e = 0; e < 4; ++e) {
+                            const float z = a[j][4 * q4 + e];
+                            r[e] = is_g ? -softplus_f(z) : sigmoid_f(z);
+                        }
+                        float* dst = is_g ? p.g + grow * p.Hv + cg0 : p.beta + grow * p.Hv + (cg0 - p.Hv);
+                        *reinterpret_cast<f32x4*>(dst) = r;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int cg = cg0 + e;
+                            const float z = a[j][4 * q4 + e];
+                            if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(z);
+                            else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(z);
+                        }
                     }
+                }
         };
         gates(acc[0], 0);
         gates(acc[1], 1);

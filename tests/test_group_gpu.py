@@ -58,9 +58,10 @@ def rel(a, b):
     return np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
 
 
-@pytest.mark.parametrize("n,with_gain", [(100, False), (130, True)])
-def test_layer_inputs_match_oracle(n, with_gain):
-    G, d, Hqk, Hv = 2, 256, 2, 4
+@pytest.mark.parametrize("n,with_gain,Hqk,Hv", [(100, False, 2, 4), (130, True, 2, 4), (77, False, 3, 6)])
+def test_layer_inputs_match_oracle(n, with_gain, Hqk, Hv):
+    # (3, 6): q and k heads share an output tile, and the gate columns are not a multiple of 4
+    G, d = 2, 256
     gi = synthetic.group_inputs(G, 1, n, d, Hqk, Hv, 128, 128, seed=3 + n, w_std=0.05, device="cuda")
     ws = [row[0] for row in gi.weights]
     if with_gain:
