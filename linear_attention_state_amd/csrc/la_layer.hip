@@ -249,27 +249,41 @@ gemm_tn_kernel(const GemmParams p)
                     *reinterpret_cast<f32x4*>(st + (32 * ii + l32) * STG_F32_ROW + 32 * j + 8 * q4 + 4 * h2) = x;
                 }
         };
+        // x_in / x_out through buffer views of this wave's rows: rows past M read as zero and
+        // their stores are dropped, so the row loop has no branches and the x_in loads can be
+        // issued before the staging.
+        const int n0 = nt * BN + wn * TN * 32 + rc;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+            const int row0 = mt * BM + wm * TM * 32 + 64 * half;
+            const int rows = max(0, min(64, p.M - row0));
+            const size_t base = ((size_t)g * p.M + row0) * p.N;
+            const uint32_t bytes = (uint32_t)rows * (uint32_t)p.N * 2u;
+            const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16*>(p.x_in + base), (short)0, (int)bytes, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+                p.x_out + base, (short)0, (int)bytes, 0x00020000);
+            bf16x8 xv[8];
+            uint32_t off[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int row = 8 * t + rr;
+                off[t] = n0 < p.N ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 2u : 0xFFFFFFF0u;
+                xv[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rin, off[t], 0, 0));
+            }
             if (half == 0) { put(acc[0], 0); put(acc[1], 1); } else { put(acc[2], 0); put(acc[3], 1); }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                const int row = 8 * t + rr;                      // 0..63
-                const int m = mt * BM + wm * TM * 32 + 64 * half + row;
-                const int n0 = nt * BN + wn * TN * 32 + rc;
+                const int row = 8 * t + rr;
                 const f32x4 v0 = *reinterpret_cast<const f32x4*>(st + row * STG_F32_ROW + rc);
                 const f32x4 v1 = *reinterpret_cast<const f32x4*>(st + row * STG_F32_ROW + rc + 4);
-                if (m < p.M && n0 < p.N) {
-                    const size_t off = ((size_t)g * p.M + m) * p.N + n0;
-                    const bf16x8 xv = *reinterpret_cast<const bf16x8*>(p.x_in + off);
-                    bf16x8 ov;
+                bf16x8 ov;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ov[e] = (bf16)((float)xv[e] + v0[e]);
-                        ov[4 + e] = (bf16)((float)xv[4 + e] + v1[e]);
-                    }
-                    *reinterpret_cast<bf16x8*>(p.x_out + off) = ov;
+                for (int e = 0; e < 4; ++e) {
+                    ov[e] = (bf16)((float)xv[t][e] + v0[e]);
+                    ov[4 + e] = (bf16)((float)xv[t][4 + e] + v1[e]);
                 }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, ov), rout, off[t], 0, 0);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next half lands
         }
