@@ -123,6 +123,19 @@ def test_group_replay_small():
     assert torch.equal(S, S2)
 
 
+def test_group_replay_more_groups_than_one_launch_takes():
+    # 18 groups: the per-group weight tables of one launch hold 16, so every stage runs as two
+    # launches; groups on both sides of the split are checked.
+    G, L, n, d, Hqk, Hv = 18, 2, 40, 128, 1, 2
+    gi = synthetic.group_inputs(G, L, n, d, Hqk, Hv, 128, 128, seed=14, w_std=0.05, device="cuda")
+    S = GroupReplay(gi.weights, n, d, Hqk, Hv, 128, 128)(gi.h_tail)
+    torch.cuda.synchronize()
+    for g in (0, 15, 16, 17):
+        ref = chain.group(np64(gi.h_tail[g:g + 1]), weights_np([gi.weights[g]]), Hqk, Hv, 128, 128)
+        err = _chain_errors(np64(S[g:g + 1]), ref)
+        assert err[0] <= 2e-3 and np.all(err[1:] <= 3e-3), (g, err)
+
+
 def test_group_replay_full_size_sampled():
     # 12 groups x 3 LA layers, d_model 2048, 16 qk / 32 v heads, m = 32768, r = 0.05
     cu, _ = tail_seqlens([32768], 5, 100)
