@@ -248,6 +248,36 @@ def time_launches(fn, steps, warmup):
     return float(np.mean(d)), float(np.median(d)), float(np.min(d))
 
 
+def time_sequence(fns, steps, warmup):
+    """Average launch duration of each fn when the sequence fns[0], fns[1], ... is repeated
+    `steps` times, every launch bracketed by its own HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    gc.collect()
+    gc.disable()
+    try:
+        _busy_gpu(torch, 0.05)
+        for row in ev:
+            for fn, (a, b) in zip(fns, row):
+                a.record(stream)
+                fn()
+                b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    out = []
+    for i in range(len(fns)):
+        d = [row[i][0].elapsed_time(row[i][1]) for row in ev]
+        out.append((float(np.mean(d)), float(np.median(d)), float(np.min(d))))
+    return out
+
+
 def _busy_gpu(torch, seconds):
     """Enqueue about `seconds` of GPU spinning on the current stream."""
     if hasattr(torch.cuda, "_sleep"):
@@ -582,20 +612,23 @@ def group_roofline(w, args):
     ws0 = [gi.weights[g][0] for g in range(G)]
     x = gi.h_tail
     y = torch.empty_like(x)
-    t_norm = time_launches(lambda: rmsnorm(x, [None] * G, y=y), reps, 2)
     out = la_project(y, ws0, Hqk, Hv, dk, dv)
-    t_proj = time_launches(lambda: la_project(y, ws0, Hqk, Hv, dk, dv, out=out), reps, 2)
     q, k, v, g, beta = out
     cu = torch.arange(G + 1, dtype=torch.int32) * n
     cu_dev = cu.to("cuda")
     S = torch.empty((G, Hv, dv, dk), dtype=torch.float32, device="cuda")
     o = torch.empty((G * n, Hv, dv), dtype=torch.bfloat16, device="cuda")
-    t_gdn_o = time_launches(lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S, o=o), reps, 2)
-    t_gdn_s = time_launches(lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S,
-                                               want_o=False), reps, 2)
     xo = torch.empty_like(x)
     o2 = o.view(G * n, Hv * dv)
-    t_out = time_launches(lambda: la_output_residual(x, o2, ws0, Hv, dv, x_out=xo), reps, 2)
+    # The kernels run in the step's order (the MFMA-heavy GEMMs between memory-bound kernels,
+    # as in the step: back to back they run hotter and clock lower), each launch timed alone.
+    t_norm, t_proj, t_gdn_o, t_out, t_gdn_s = time_sequence([
+        lambda: rmsnorm(x, [None] * G, y=y),
+        lambda: la_project(y, ws0, Hqk, Hv, dk, dv, out=out),
+        lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S, o=o),
+        lambda: la_output_residual(x, o2, ws0, Hv, dv, x_out=xo),
+        lambda: gdn_replay(q, k, v, g, beta, cu, cu_seqlens_dev=cu_dev, state_out=S, want_o=False),
+    ], reps, 2)
 
     proj_flops = 2.0 * G * n * d * (2 * Hqk * dk + Hv * dv + 2 * Hv)
     out_flops = 2.0 * G * n * Hv * dv * d
