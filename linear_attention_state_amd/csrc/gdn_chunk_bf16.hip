@@ -51,6 +51,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -547,20 +548,22 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                             lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * ct + tr_c]));
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
+                // W^T tile (operands swapped): lane (t = l32, h) holds token 32 rt + t, dk columns
+                // 32 ct + 8 q + 4 h + {0..3} -- 8-byte row segments of -W
                 f32x16 acc = zero16();
 #pragma unroll
                 for (int s = 0; s < 2 * rt + 2; ++s)
-                    acc = mma32(kperm(&sm.np.n.Nbg[32 * rt + l32][0], s, h2), kb[s], acc);
+                    acc = mma32(kb[s], kperm(&sm.np.n.Nbg[32 * rt + l32][0], s, h2), acc);
+                const int t = 32 * rt + l32;
+                const float bgt = sm.bg[t];
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const int t4 = 32 * rt + 8 * j4 + 4 * h2;
-                    const f32x4 bg = tab4(sm.bg, t4);
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 32 * ct + 8 * q + 4 * h2;
+                    const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&sm.K[t][c]);
+                    bf16x4 w;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = 4 * j4 + e;
-                        const float w = acc[j] + bg[e] * (float)kb[2 * rt + (j >> 3)][j & 7];
-                        sm.lw.Wn[t4 + e][32 * ct + l32] = (bf16)(-w);
-                    }
+                    for (int e = 0; e < 4; ++e) w[e] = (bf16)(-(acc[4 * q + e] + bgt * (float)kt[e]));
+                    *reinterpret_cast<bf16x4*>(&sm.lw.Wn[t][c]) = w;
                 }
             }
         }
