@@ -164,7 +164,7 @@ def build_workload(name, seed):
 def make_step(w):
     """Returns step() that runs tail selection + the replay call(s) on the current stream."""
     import torch
-    from linear_attention_state_amd import GroupReplay, gdn_replay, tail_seqlens
+    from linear_attention_state_amd import GroupReplay, gdn_replay, gdn_replay_workspace_size, tail_seqlens
 
     rn, rd = w["r"]
     if w["kind"] == "gdn":
@@ -172,10 +172,15 @@ def make_step(w):
         B, Hv, dk, dv = len(w["lens"]), spec["Hv"], spec["dk"], spec["dv"]
         S = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device="cuda")
         o = torch.empty((inp.q.shape[0], Hv, dv), dtype=torch.bfloat16, device="cuda")
+        # the split schedule's workspace, allocated once outside the timed steps
+        cu0, _ = tail_seqlens(w["ms"], rn, rd)
+        nws = gdn_replay_workspace_size(cu0, spec["Hqk"], Hv, dk, dv, torch.bfloat16)
+        w["workspace"] = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
 
         def step():
             cu, _ = tail_seqlens(w["ms"], rn, rd)
-            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
+            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o,
+                       workspace=w["workspace"])
         return step, (S, o)
     spec, gi = w["spec"], w["inputs"]
     runner = GroupReplay(gi.weights, w["n"], spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
@@ -545,9 +550,15 @@ def main():
         cu_host = torch.from_numpy(np.concatenate([[0], np.cumsum(w["lens"])]).astype(np.int32))
 
         def kern():
-            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_host, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
+            gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_host, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o,
+                       workspace=w["workspace"])
         k_mean, k_med, k_min = time_launches(kern, max(args.steps, 10), 2)
-        kname = "gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"])
+        if w["workspace"] is None:
+            kname = "gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"])
+        else:
+            # split schedule: one tr_gdn_replay call is the prep kernel then the state scan
+            kname = "gdn split schedule <%d,%d> (gdn_chunk_bf16_kernel prep + gdn_scan_split_kernel)" % (
+                spec["dk"], spec["dv"])
         roof = dict(bound="hbm", achieved=nbytes / (k_mean * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                     traffic=measured_traffic(kname, args.workload), kernel=kname,
                     algorithmic_bytes=nbytes, avg_launch_us=k_mean * 1e3, median_launch_us=k_med * 1e3,

@@ -48,6 +48,12 @@ typedef enum {
     TR_F32 = 1                /* q, k, v, o in fp32; fp32 arithmetic throughout */
 } tr_dtype;
 
+typedef enum {
+    TR_SCHEDULE_AUTO = 0,     /* split when the request has few heads (the default) */
+    TR_SCHEDULE_FUSED = 1,    /* always one workgroup per (sequence, value head) */
+    TR_SCHEDULE_SPLIT = 2     /* always the split schedule (bf16) */
+} tr_schedule;
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* tr_last_error(void);
 
@@ -100,8 +106,20 @@ tr_status tr_tail_seqlens(const int64_t* m_host, int32_t B, int32_t r_num, int32
  *   state_out   [device] [B, Hv, dv, dk] fp32; may equal state_in
  *   o           [device] [T, Hv, dv] dtype `dt`, or NULL to skip the per-token outputs
  *               (state-only mode)
+ *   workspace   [device] scratch of at least tr_gdn_replay_workspace_size() bytes for this
+ *               request, 16-byte aligned; may be NULL when that size is 0.  Contents on
+ *               entry do not matter; the call overwrites them.
+ *   workspace_bytes  its size
  *   stream      hipStream_t to enqueue on
+ * Schedules (bf16): the fused schedule runs one workgroup per (sequence, value head) and
+ * needs no workspace.  With few heads that leaves most of the chip idle, so the split
+ * schedule (default for at most 256 / (dv / 32) heads in all) first runs every chunk's
+ * state-free part in parallel -- gate cumsum, K K^T, (I + L)^{-1}, W, U0, Q K^T -- into the
+ * workspace, then the state scan with each state split along dv across workgroups (rows of S
+ * evolve independently, section 2.3).  Both give the same results to within rounding.
  * Supported: dk, dv in {64, 128}.  Empty sequences copy state_in (or write zeros).
+ * Errors: TR_ERR_INVALID_ARG (sizes, pointers, cu_seqlens), TR_ERR_UNSUPPORTED (head
+ *   dims), TR_ERR_WORKSPACE (workspace NULL or smaller than needed), TR_ERR_HIP.
  * Numerics: keys with beta |k|^2 <= 2 keep the operator non-expanding (reading notes,
  *   section 2.3); far outside that the recurrence itself grows without bound.
  * ------------------------------------------------------------------------------- */
@@ -111,7 +129,18 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
                         tr_dtype dt, float q_scale,
                         const float* state_in, float* state_out, void* o,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace tr_gdn_replay needs for this request under the current schedule
+ * (0 when it needs none).  Arguments as for tr_gdn_replay; T is cu_seqlens_host[B].
+ * Returns 0 and sets tr_last_error() for invalid arguments. */
+size_t tr_gdn_replay_workspace_size(const int32_t* cu_seqlens_host, int32_t B, int32_t Hqk, int32_t Hv,
+                                    int32_t dk, int32_t dv, tr_dtype dt);
+
+/* Process-wide schedule of tr_gdn_replay's bf16 path (TR_SCHEDULE_AUTO at load).  Query the
+ * workspace size after changing it.  Returns TR_ERR_INVALID_ARG for an unknown value. */
+tr_status tr_gdn_set_schedule(tr_schedule schedule);
+tr_schedule tr_gdn_get_schedule(void);
 
 /* ---------------------------------------------------------------------------------
  * tr_gdn_transition -- the product of the transition operators of a replayed span.

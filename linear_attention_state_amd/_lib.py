@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libtailreplay.so")
 
 TR_OK, TR_ERR_INVALID_ARG, TR_ERR_UNSUPPORTED, TR_ERR_WORKSPACE, TR_ERR_HIP = range(5)
 TR_BF16, TR_F32 = 0, 1
+TR_SCHEDULE_AUTO, TR_SCHEDULE_FUSED, TR_SCHEDULE_SPLIT = 0, 1, 2
 
 # Every symbol the header declares: (name, restype, argtypes).
 _vp = ctypes.c_void_p
@@ -34,7 +35,10 @@ SIGNATURES = {
     "tr_tail_seqlens": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "tr_gdn_replay": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
-                                     _vp, _vp, _vp, _vp]),
+                                     _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tr_gdn_replay_workspace_size": (_sz, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]),
+    "tr_gdn_set_schedule": (ctypes.c_int, [ctypes.c_int]),
+    "tr_gdn_get_schedule": (ctypes.c_int, []),
     "tr_gdn_transition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                                          _vp, _vp, _vp]),
     "tr_state_compose": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),

@@ -3,6 +3,7 @@
 // first HIP call, so a rejected request enqueues nothing.
 #include "tailreplay.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -210,8 +211,32 @@ tr_status check_gdn(const char* fn, const int32_t* cu_seqlens_host, const int32_
     }
     if (cu_seqlens_host[B] != T)
         return fail(TR_ERR_INVALID_ARG, "%s: cu_seqlens[B] = %d but T = %d", fn, cu_seqlens_host[B], T);
+    // the kernels address one sequence's rows with 32-bit byte offsets
+    const int64_t esize = dt == TR_BF16 ? 2 : 4;
+    if ((int64_t)ml * std::max((int64_t)Hqk * dk, (int64_t)Hv * dv) * esize > INT32_MAX)
+        return fail(TR_ERR_INVALID_ARG, "%s: a sequence of %d tokens is too long for these head sizes", fn, ml);
     *max_len = ml;
     return TR_OK;
+}
+
+// Schedule of the bf16 recurrence (tr_gdn_set_schedule).  The split schedule is chosen
+// automatically when the fused one would leave most of the chip idle: at most
+// kSplitMaxWaves state-scan waves (32 value columns each).
+std::atomic<int> g_schedule{TR_SCHEDULE_AUTO};
+constexpr int64_t kSplitMaxWaves = 256;
+
+bool use_split(int32_t B, int32_t Hv, int32_t dv, tr_dtype dt) {
+    if (dt != TR_BF16) return false;
+    const int s = g_schedule.load(std::memory_order_relaxed);
+    if (s == TR_SCHEDULE_FUSED) return false;
+    if (s == TR_SCHEDULE_SPLIT) return true;
+    return (int64_t)B * Hv * (dv / 32) <= kSplitMaxWaves;
+}
+
+int64_t split_records_per_head(int32_t B, int32_t T) { return ((int64_t)T + 63) / 64 + B; }
+
+size_t split_workspace_bytes(int32_t B, int32_t T, int32_t Hv, int32_t dk, int32_t dv) {
+    return (size_t)Hv * (size_t)split_records_per_head(B, T) * tr::split_record_bytes(dk, dv);
 }
 
 hipError_t launch_gdn(const tr::GdnArgs& a, tr_dtype dt, hipStream_t s) {
@@ -222,13 +247,34 @@ hipError_t launch_gdn(const tr::GdnArgs& a, tr_dtype dt, hipStream_t s) {
 
 extern "C" {
 
+tr_status tr_gdn_set_schedule(tr_schedule schedule) {
+    if (schedule != TR_SCHEDULE_AUTO && schedule != TR_SCHEDULE_FUSED && schedule != TR_SCHEDULE_SPLIT)
+        return fail(TR_ERR_INVALID_ARG, "tr_gdn_set_schedule: unknown schedule %d", (int)schedule);
+    g_schedule.store((int)schedule, std::memory_order_relaxed);
+    return ok();
+}
+
+tr_schedule tr_gdn_get_schedule(void) { return (tr_schedule)g_schedule.load(std::memory_order_relaxed); }
+
+size_t tr_gdn_replay_workspace_size(const int32_t* cu_seqlens_host, int32_t B, int32_t Hqk, int32_t Hv,
+                                    int32_t dk, int32_t dv, tr_dtype dt) {
+    static const char* fn = "tr_gdn_replay_workspace_size";
+    if (!cu_seqlens_host || B < 1) { fail(TR_ERR_INVALID_ARG, "%s: need cu_seqlens_host and B >= 1", fn); return 0; }
+    int32_t max_len = 0;
+    // the device copy is not needed here: pass the host array for the null check
+    if (check_gdn(fn, cu_seqlens_host, cu_seqlens_host, B, cu_seqlens_host[B], Hqk, Hv, dk, dv, dt, &max_len) != TR_OK)
+        return 0;
+    ok();
+    return use_split(B, Hv, dv, dt) ? split_workspace_bytes(B, cu_seqlens_host[B], Hv, dk, dv) : 0;
+}
+
 tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         const float* g, const float* beta,
                         const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
                         int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
                         tr_dtype dt, float q_scale,
                         const float* state_in, float* state_out, void* o,
-                        void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream) {
     static const char* fn = "tr_gdn_replay";
     int32_t max_len = 0;
     const tr_status st = check_gdn(fn, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, dk, dv, dt, &max_len);
@@ -237,6 +283,14 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
         return fail(TR_ERR_INVALID_ARG, "%s: q_scale must be finite and > 0", fn);
     if (!state_out) return fail(TR_ERR_INVALID_ARG, "%s: null state_out", fn);
     if (T > 0 && (!q || !k || !v || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
+    const bool split = use_split(B, Hv, dv, dt);
+    const size_t need = split ? split_workspace_bytes(B, T, Hv, dk, dv) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace ? workspace_bytes : (size_t)0, need);
+    if (need > 0 && ((uintptr_t)workspace & 15) != 0)
+        return fail(TR_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+    if (split && (int64_t)((max_len + 63) / 64) * (int64_t)tr::split_record_bytes(dk, dv) > INT32_MAX)
+        return fail(TR_ERR_INVALID_ARG, "%s: a sequence of %d tokens is too long for the split schedule", fn, max_len);
 
     tr::GdnArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens_dev;
@@ -245,7 +299,15 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     a.log_scale_out = nullptr;
     a.uniform_len = 0; a.state_bstride = (int64_t)Hv * dv * dk;
     hipStream_t s = (hipStream_t)stream;
-    return finish_launch(launch_gdn(a, dt, s), s, fn);
+    if (!split) return finish_launch(launch_gdn(a, dt, s), s, fn);
+    // split schedule: chunk-parallel prep into the workspace, then the state scan split along dv
+    tr::SplitPlan plan;
+    plan.ws = workspace;
+    plan.rec_per_head = split_records_per_head(B, T);
+    plan.cmax = (max_len + 63) / 64;
+    hipError_t e = plan.cmax > 0 ? tr::launch_gdn_prep_bf16(a, plan, s) : hipSuccess;
+    if (e == hipSuccess) e = tr::launch_gdn_scan_split_bf16(a, plan, s);
+    return finish_launch(e, s, fn);
 }
 
 tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,

@@ -40,6 +40,12 @@
 //       update S <- e^{gamma_n} S + U'^T D K and O = e^gamma q_scale Y + P U' share the
 //       token k-steps (independent accumulators); O stored
 // The state-only variant (WITH_O = false) drops Q, Q K^T, P and O.
+//
+// PREP = true is the first kernel of the split schedule (few heads): one workgroup per
+// (sequence, chunk, value head) runs P0-P4 only -- nothing there depends on the state -- and
+// writes the chunk's operands -W, K^T, P hi / lo, U0 and the gate tables to a record in the
+// workspace as MFMA operand fragments; gdn_scan_split.hip then runs the state part with the
+// state split along dv.
 // An accumulator feeds the next product directly as its B operand: the contraction index
 // is permuted the same way on both operands (see kperm()).
 #include "internal.h"
@@ -195,13 +201,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // WITH_O: per-token outputs are produced (Q is loaded, Q K^T and P formed, O stored); without
 // them the kernel is the state-only scan.
-template <int DK, int DV, bool WITH_O>
+template <int DK, int DV, bool WITH_O, bool PREP>
 __global__ void __launch_bounds__(DV * 2, 2)
 gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
                       int B, int Hqk, int Hv, float q_scale, int uniform_len, long long state_bstride,
-                      const float* state_in, int state_identity, float* state_out, bf16* __restrict__ o)
+                      const float* state_in, int state_identity, float* state_out, bf16* __restrict__ o,
+                      unsigned char* __restrict__ ws, long long rec_per_head, int cmax)
 {
     constexpr int NW = DV / 32;            // waves; wave w owns dv columns [32w, 32w+32)
     constexpr int NT = NW * 64;
@@ -236,13 +243,17 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // reader of each key/query tile finds it in that XCD's L2.
     const int per_xcd = (int)(gridDim.x / 8);
     const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if (item >= B * Hv) return;
-    const int b = item / Hv;
+    // PREP items are (sequence, chunk, value head), value head fastest
+    if (item >= B * Hv * (PREP ? cmax : 1)) return;
+    const int b = PREP ? item / (Hv * cmax) : item / Hv;
     const int hv = item % Hv;
     const int hq = hv / (Hv / Hqk);
     const int bos = cu ? cu[b] : b * uniform_len;
     const int len = cu ? cu[b + 1] - bos : uniform_len;
     const int n_chunks = (len + CH - 1) / CH;
+    const int c_begin = PREP ? (item / Hv) % cmax : 0;
+    const int c_end = PREP ? c_begin + 1 : n_chunks;
+    if (PREP && c_begin >= n_chunks) return;
     const int col0 = 32 * wave;
 
     // Buffer views of this (sequence, head): rows past the sequence end read as zero.
@@ -264,6 +275,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const size_t sbase = (size_t)b * state_bstride + (size_t)hv * DV * DK + (size_t)(col0 + l32) * DK;
 #pragma unroll
     for (int r = 0; r < KT_TILES; ++r) {
+        if (PREP) break;
         if (state_identity) {
             // S = I: element (dv col0 + l32, dk 32 r + 8 q4 + 4 h2 + i)
 #pragma unroll
@@ -310,9 +322,9 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * gb_stride, soff, 0));
         }
     };
-    if (n_chunks > 0) fetch_kq(0);
+    if (c_begin < c_end) fetch_kq(c_begin);
 
-    for (int c = 0; c < n_chunks; ++c) {
+    for (int c = c_begin; c < c_end; ++c) {
         // Recompute the lane-derived indices every chunk: left loop-invariant, the compiler
         // hoists dozens of per-lane LDS addresses out of the loop and spills them.
         asm volatile("" : "+v"(lane));
@@ -362,7 +374,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 }
         }
 
-        if (c + 1 < n_chunks) fetch_kq(c + 1);
+        if (c + 1 < c_end) fetch_kq(c + 1);
         lds_barrier();
 
         // ------------------------------------------------------------- P1: K K^T -> L
@@ -569,6 +581,40 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
         lds_barrier();
 
+        unsigned char* rec = nullptr;
+        if constexpr (PREP) {
+            // the chunk's record: operand fragments, 64 lanes x 16 bytes each
+            rec = ws + ((size_t)hv * rec_per_head + (size_t)(bos / CH + b + c)) * split_record_bytes(DK, DV);
+            for (int f = wave; f < 2 * KSTEPS_D; f += NW) {          // -W and Q, (row tile, k-step)
+                const int rt = f / KSTEPS_D, s = f % KSTEPS_D;
+                *reinterpret_cast<bf16x8*>(rec + split_wn_off() + (size_t)(f * 64 + lane) * 16) =
+                    kperm(&sm.lw.Wn[32 * rt + l32][0], s, h2);
+                if (WITH_O)
+                    *reinterpret_cast<bf16x8*>(rec + split_q_off(DK) + (size_t)(f * 64 + lane) * 16) =
+                        kperm(&sm.Q[32 * rt + l32][0], s, h2);
+            }
+            for (int f = wave; f < 4 * KT_TILES; f += NW) {          // K^T, (token k-step, dk tile)
+                const int s = f / KT_TILES, r = f % KT_TILES;
+                *reinterpret_cast<bf16x8*>(rec + split_kt_off(DK) + (size_t)(f * 64 + lane) * 16) =
+                    cat(lds_tr4(&sm.K[16 * s + 4 * h2 + tr_p][32 * r + tr_c]),
+                        lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * r + tr_c]));
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)                           // U0 of this wave's columns
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = U[rt][4 * q4 + i];
+                    *reinterpret_cast<f32x4*>(rec + split_u0_off(DK) + (size_t)((wave * 2 + rt) * 64 + lane) * 64 + q4 * 16) = x;
+                }
+            if (tid < CH) {
+                const int row = tid / 16, i4 = 4 * (tid % 16);
+                const float* t = row == 0 ? sm.bt : (row == 1 ? sm.qeg : (row == 2 ? sm.dec : sm.eg));
+                *reinterpret_cast<f32x4*>(rec + split_tab_off(DK, DV) + (row * CH + i4) * 4) = tab4(t, i4);
+            }
+        }
+
         // ------------------------------------------------------------ P4: P to LDS
         if (WITH_O) {
 #pragma unroll
@@ -604,6 +650,19 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                 }
         }
         lds_barrier();
+
+        if constexpr (PREP) {
+            if (WITH_O) {
+                for (int f = wave; f < 12; f += NW) {       // P hi then lo, (rt, s) with s < 2 rt + 2
+                    const int hl = f / 6, ff = f % 6;
+                    const int rt = ff < 2 ? 0 : 1, s = ff < 2 ? ff : ff - 2;
+                    const bf16* row = hl ? &sm.np.p.Pl[32 * rt + l32][0] : &sm.np.p.Ph[32 * rt + l32][0];
+                    *reinterpret_cast<bf16x8*>(rec + (hl ? split_pl_off(DK) : split_ph_off(DK)) + (size_t)(ff * 64 + lane) * 16) =
+                        kperm(row, s, h2);
+                }
+            }
+            continue;
+        }
 
         // ------------------------------------------------ P5: state-dependent part
         // U' = U0 + (-W) S^T and, with outputs, Y = Q S^T: one conversion of each state operand
@@ -691,6 +750,7 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 
     // ---- write the final state
+    if (PREP) return;
 #pragma unroll
     for (int r = 0; r < KT_TILES; ++r) {
 #pragma unroll
@@ -703,34 +763,47 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
 }
 
-template <int DK, int DV, bool WITH_O>
-hipError_t launch_variant(const GdnArgs& a, hipStream_t stream) {
-    auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O>;
+template <int DK, int DV, bool WITH_O, bool PREP>
+hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
+    auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O, PREP>;
     const size_t smem = sizeof(Smem<DK, DV>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((a.B * a.Hv + 7) / 8 * 8));    // a multiple of 8: one share per XCD
+    const long long items = (long long)a.B * a.Hv * (PREP ? plan->cmax : 1);
+    const dim3 grid((unsigned)((items + 7) / 8 * 8));    // a multiple of 8: one share per XCD
     const dim3 block(DV * 2);
     hipLaunchKernelGGL(kern, grid, block, smem, stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
                        a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
-                       a.state_in, a.state_identity, a.state_out, (bf16*)a.o);
+                       a.state_in, a.state_identity, a.state_out, (bf16*)a.o,
+                       PREP ? (unsigned char*)plan->ws : nullptr, PREP ? (long long)plan->rec_per_head : 0LL,
+                       PREP ? plan->cmax : 0);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
-hipError_t launch(const GdnArgs& a, hipStream_t stream) {
-    return a.o ? launch_variant<DK, DV, true>(a, stream) : launch_variant<DK, DV, false>(a, stream);
+template <int DK, int DV, bool PREP>
+hipError_t launch(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
+    return a.o ? launch_variant<DK, DV, true, PREP>(a, plan, stream)
+               : launch_variant<DK, DV, false, PREP>(a, plan, stream);
+}
+
+template <bool PREP>
+hipError_t launch_dims(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
+    if (a.dk == 128 && a.dv == 128) return launch<128, 128, PREP>(a, plan, stream);
+    if (a.dk == 64 && a.dv == 64) return launch<64, 64, PREP>(a, plan, stream);
+    if (a.dk == 128 && a.dv == 64) return launch<128, 64, PREP>(a, plan, stream);
+    if (a.dk == 64 && a.dv == 128) return launch<64, 128, PREP>(a, plan, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream) {
-    if (a.dk == 128 && a.dv == 128) return launch<128, 128>(a, stream);
-    if (a.dk == 64 && a.dv == 64) return launch<64, 64>(a, stream);
-    if (a.dk == 128 && a.dv == 64) return launch<128, 64>(a, stream);
-    if (a.dk == 64 && a.dv == 128) return launch<64, 128>(a, stream);
-    return hipErrorInvalidValue;
+    return launch_dims<false>(a, nullptr, stream);
+}
+
+hipError_t launch_gdn_prep_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream) {
+    return launch_dims<true>(a, &plan, stream);
 }
 
 }  // namespace tr

@@ -31,6 +31,36 @@ struct GdnArgs {
 
 // Chunked WY-form recurrence, bf16 operands, fp32 state (gdn_chunk_bf16.hip).
 hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream);
+
+// Split schedule for few heads: a chunk-parallel prep kernel writes one record per
+// (value head, chunk) to the workspace, then the state scan runs with each state split
+// along dv across workgroups (gdn_scan_split.hip).  A record holds MFMA operand fragments
+// of the 32x32x16 bf16 layouts: fragment = 64 lanes x 16 bytes, lane l's 8 values in the
+// order the operand takes them (row or column l % 32, contraction 16 s + 4 h + {0..3},
+// 16 s + 8 + 4 h + {0..3}, h = l / 32).  In order, bytes:
+//   -W          [row tile rt < 2][k-step s < dk/16]          (A operand of -W S^T)
+//   Q           [row tile rt < 2][k-step s < dk/16]          (B operand of S Q^T)
+//   K^T         [k-step s < 4][dk tile r < dk/32]            (A operand of the state update)
+//   P hi, P lo  [(rt, s), s < 2 rt + 2: 6 fragments] each    (B operand of (P U')^T)
+//   U0          [dv tile w < dv/32][rt < 2][lane][16 fp32]   (accumulator registers)
+//   tables      [4][64] fp32: beta, q_scale e^gamma, e^{gamma_last - gamma}, e^gamma
+// Records of sequence b sit at index floor(cu[b] / 64) + b + chunk within each head, which
+// never collide and stay below ceil(T / 64) + B.
+constexpr size_t split_wn_off() { return 0; }
+constexpr size_t split_q_off(int dk) { return (size_t)dk * 128; }
+constexpr size_t split_kt_off(int dk) { return split_q_off(dk) + (size_t)dk * 128; }
+constexpr size_t split_ph_off(int dk) { return split_kt_off(dk) + (size_t)dk * 128; }
+constexpr size_t split_pl_off(int dk) { return split_ph_off(dk) + 6 * 1024; }
+constexpr size_t split_u0_off(int dk) { return split_pl_off(dk) + 6 * 1024; }
+constexpr size_t split_tab_off(int dk, int dv) { return split_u0_off(dk) + (size_t)dv * 256; }
+constexpr size_t split_record_bytes(int dk, int dv) { return split_tab_off(dk, dv) + 4 * 64 * 4; }
+struct SplitPlan {
+    void* ws;                    // records, [Hv][rec_per_head]
+    int64_t rec_per_head;        // ceil(T / 64) + B
+    int32_t cmax;                // most chunks in one sequence
+};
+hipError_t launch_gdn_prep_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
+hipError_t launch_gdn_scan_split_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
 // Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
 hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream);
 // The same fp32 arithmetic on bf16 inputs (and bf16 outputs).

@@ -48,12 +48,38 @@ def tail_seqlens(m: Sequence[int], r_num: int, r_den: int):
     return cu, starts
 
 
+_SCHEDULES = {"auto": 0, "fused": 1, "split": 2}
+
+
+def set_gdn_schedule(schedule: str) -> None:
+    """Process-wide schedule of the bf16 recurrence: "auto" (split for few heads), "fused"
+    or "split" (tr_gdn_set_schedule)."""
+    _need(schedule in _SCHEDULES, "schedule must be one of %s" % sorted(_SCHEDULES))
+    check(lib().tr_gdn_set_schedule(_SCHEDULES[schedule]))
+
+
+def get_gdn_schedule() -> str:
+    code = lib().tr_gdn_get_schedule()
+    return {v: k for k, v in _SCHEDULES.items()}[code]
+
+
+def gdn_replay_workspace_size(cu_seqlens, Hqk: int, Hv: int, dk: int, dv: int, dtype) -> int:
+    """Bytes of workspace tr_gdn_replay needs for this request (0 for none)."""
+    cu = cu_seqlens.to(torch.int32).cpu().contiguous()
+    n = lib().tr_gdn_replay_workspace_size(_ptr(cu), cu.numel() - 1, Hqk, Hv, dk, dv, _DT[dtype])
+    msg = lib().tr_last_error().decode()
+    _need(not msg, msg)
+    return int(n)
+
+
 def gdn_replay(q, k, v, g, beta, cu_seqlens, q_scale: float = 1.0, state_in=None,
-               want_o: bool = True, cu_seqlens_dev=None, state_out=None, o=None, stream=None):
+               want_o: bool = True, cu_seqlens_dev=None, state_out=None, o=None, workspace=None, stream=None):
     """Varlen GDN recurrence (tr_gdn_replay).  Returns (state_out [B,Hv,dv,dk] fp32, o or None).
 
     q, k [T, Hqk, dk], v [T, Hv, dv] in bf16 (chunked MFMA path) or fp32; g, beta [T, Hv]
     fp32; cu_seqlens [B+1] int32 on the host; state_in optional [B, Hv, dv, dk] fp32.
+    workspace: a uint8 device tensor of at least gdn_replay_workspace_size() bytes, or None
+    to allocate one when the schedule needs it.
     """
     _need(q.is_cuda and k.is_cuda and v.is_cuda and g.is_cuda and beta.is_cuda, "inputs must be on the GPU")
     _need(q.dtype == k.dtype == v.dtype and q.dtype in _DT, "q, k, v must share dtype bf16 or fp32")
@@ -78,9 +104,17 @@ def gdn_replay(q, k, v, g, beta, cu_seqlens, q_scale: float = 1.0, state_in=None
         o = torch.empty((T, Hv, dv), dtype=q.dtype, device=q.device)
     if not want_o:
         o = None
+    if workspace is None:
+        need = lib().tr_gdn_replay_workspace_size(_ptr(cu), B, Hqk, Hv, dk, dv, _DT[q.dtype])
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
     st = lib().tr_gdn_replay(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu), _ptr(cu_seqlens_dev),
                              B, T, Hqk, Hv, dk, dv, _DT[q.dtype], float(q_scale),
-                             _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream))
+                             _ptr(state_in), _ptr(state_out), _ptr(o), _ptr(workspace), ws_bytes, _stream(stream))
     check(st)
     return state_out, o
 

@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tailreplay.h")
 
 L = pytest.importorskip("linear_attention_state_amd")
+from linear_attention_state_amd import _lib as C  # noqa: E402  (status and schedule codes)
 
 
 def declared_functions():
@@ -61,12 +62,14 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 def call_gdn(**over):
     cu = (ctypes.c_int32 * 3)(0, 5, 9)
     args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu_h=ctypes.cast(cu, ctypes.c_void_p), cu_d=FAKE,
-                B=2, T=9, Hqk=2, Hv=4, dk=128, dv=128, dt=0, q_scale=1.0, s_in=None, s_out=FAKE, o=FAKE)
+                B=2, T=9, Hqk=2, Hv=4, dk=128, dv=128, dt=0, q_scale=1.0, s_in=None, s_out=FAKE, o=FAKE,
+                ws=None, ws_bytes=0)
     args.update(over)
     lib = L.lib()
     st = lib.tr_gdn_replay(args["q"], args["k"], args["v"], args["g"], args["beta"], args["cu_h"], args["cu_d"],
                            args["B"], args["T"], args["Hqk"], args["Hv"], args["dk"], args["dv"], args["dt"],
-                           args["q_scale"], args["s_in"], args["s_out"], args["o"], None)
+                           args["q_scale"], args["s_in"], args["s_out"], args["o"], args["ws"], args["ws_bytes"],
+                           None)
     return st, lib.tr_last_error().decode()
 
 
@@ -88,6 +91,42 @@ def call_gdn(**over):
 def test_gdn_rejects_bad_arguments(over, status):
     st, msg = call_gdn(**over)
     assert st == status and msg
+
+
+def _ws_size(cu, B, Hv=4, dv=128, dt=0):
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    return L.lib().tr_gdn_replay_workspace_size(ctypes.cast(arr, ctypes.c_void_p), B, 2, Hv, 128, dv, dt)
+
+
+def test_gdn_schedule_and_workspace_query():
+    lib = L.lib()
+    prev = lib.tr_gdn_get_schedule()
+    try:
+        assert lib.tr_gdn_set_schedule(7) == C.TR_ERR_INVALID_ARG and lib.tr_last_error()
+        assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_AUTO) == C.TR_OK
+        assert lib.tr_gdn_get_schedule() == C.TR_SCHEDULE_AUTO
+        # few heads: the split schedule, whose records grow with the chunks and the heads
+        n1 = _ws_size([0, 5, 9], 2)
+        n2 = _ws_size([0, 500, 900], 2)
+        assert 0 < n1 < n2 and n2 % 16 == 0
+        assert _ws_size([0, 5, 9], 2, Hv=8) == 2 * n1
+        assert _ws_size([0, 5, 9], 2, dt=1) == 0            # fp32 inputs: token path, no workspace
+        assert _ws_size([0, 5, 9], 2, Hv=128) == 0          # many heads: fused
+        assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_FUSED) == C.TR_OK
+        assert _ws_size([0, 5, 9], 2) == 0
+        assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_SPLIT) == C.TR_OK
+        assert _ws_size([0, 5, 9], 2, Hv=128) > 0
+        assert _ws_size([0, 5, 9], 0) == 0 and lib.tr_last_error()   # invalid: B = 0
+        # a missing or short workspace is rejected before anything is enqueued
+        assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_AUTO) == C.TR_OK
+        st, msg = call_gdn()
+        assert st == C.TR_ERR_WORKSPACE and "workspace" in msg
+        st, msg = call_gdn(ws=FAKE, ws_bytes=n1 - 1)
+        assert st == C.TR_ERR_WORKSPACE
+        st, msg = call_gdn(ws=ctypes.c_void_p(0x1008), ws_bytes=n1)
+        assert st == C.TR_ERR_INVALID_ARG and "aligned" in msg
+    finally:
+        lib.tr_gdn_set_schedule(prev)
 
 
 def test_gdn_rejects_bad_cu_seqlens():

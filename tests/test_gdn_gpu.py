@@ -4,6 +4,9 @@ Tolerances (relative Frobenius error of every (sequence, value head) slice, comp
 fp64): bf16 inputs with fp32 state -- states <= 2e-3, outputs <= 3e-3; fp32 inputs --
 <= 1e-5 for both.  Outputs are compared as stored (bf16 for bf16 inputs), so the output
 bound includes the bf16 rounding of o itself (about 1.7e-3 relative).
+
+The bf16 cases run under both schedules (fixture `schedule`): the fused kernel, and the
+split one (chunk-parallel prep, then the state scan split along dv across workgroups).
 """
 import numpy as np
 import pytest
@@ -11,11 +14,19 @@ import torch
 
 import oracle
 import synthetic
-from linear_attention_state_amd import gdn_replay, tail_seqlens
+from linear_attention_state_amd import gdn_replay, get_gdn_schedule, set_gdn_schedule, tail_seqlens
 
 pytestmark = pytest.mark.gpu
 
 STATE_TOL, OUT_TOL, F32_TOL = 2e-3, 3e-3, 1e-5
+
+
+@pytest.fixture(params=["fused", "split"])
+def schedule(request):
+    prev = get_gdn_schedule()
+    set_gdn_schedule(request.param)
+    yield request.param
+    set_gdn_schedule(prev)
 
 
 def rel(a, b):
@@ -69,17 +80,17 @@ RAGGED = [1, 63, 64, 65, 130, 0, 200, 7]
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-def test_bf16_ragged_zero_state(dk, dv):
+def test_bf16_ragged_zero_state(dk, dv, schedule):
     inp = synthetic.gdn_inputs(RAGGED, 2, 4, dk, dv, seed=100 + dk + dv)
-    run_and_compare(inp, label="bf16 ragged %dx%d" % (dk, dv))
+    run_and_compare(inp, label="bf16 ragged %dx%d %s" % (dk, dv, schedule))
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
-def test_bf16_ragged_given_state_and_scale(dk, dv):
+def test_bf16_ragged_given_state_and_scale(dk, dv, schedule):
     inp = synthetic.gdn_inputs(RAGGED, 1, 3, dk, dv, seed=7 + dk, q_prescaled=False)
     rng = np.random.default_rng(5)
     s_in = (rng.standard_normal((len(RAGGED), 3, dv, dk)) * 0.3).astype(np.float32)
-    run_and_compare(inp, state_in=s_in, q_scale=dk ** -0.5, label="bf16 state_in %dx%d" % (dk, dv))
+    run_and_compare(inp, state_in=s_in, q_scale=dk ** -0.5, label="bf16 state_in %dx%d %s" % (dk, dv, schedule))
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
@@ -90,11 +101,11 @@ def test_fp32_ragged(dk, dv):
     run_and_compare(inp, state_in=s_in, q_scale=0.5, stol=F32_TOL, otol=F32_TOL, label="fp32 ragged")
 
 
-def test_single_hit_full_size():
+def test_single_hit_full_size(schedule):
     # m = 32768, r = 0.05 -> 1,639 tokens, 16 heads, dk = dv = 128, zero state
     cu, _ = tail_seqlens([32768], 5, 100)
     inp = synthetic.gdn_inputs([int(cu[1])], 16, 16, 128, 128, seed=2)
-    run_and_compare(inp, label="single hit")
+    run_and_compare(inp, label="single hit %s" % schedule)
 
 
 def _sampled_parity(inp_dev, cu, seqs, heads, Hqk, Hv, S, o):
@@ -138,7 +149,7 @@ def test_varlen_full_size_sampled():
     assert es <= STATE_TOL and eo <= OUT_TOL
 
 
-def test_packed_equals_separate_calls_bitwise():
+def test_packed_equals_separate_calls_bitwise(schedule):
     lens = [70, 1, 129]
     inp = synthetic.gdn_inputs(lens, 2, 4, 128, 128, seed=44).to("cuda")
     S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
@@ -151,7 +162,7 @@ def test_packed_equals_separate_calls_bitwise():
         assert torch.equal(ob, o[sl])
 
 
-def test_deterministic_and_state_only_and_in_place():
+def test_deterministic_and_state_only_and_in_place(schedule):
     inp = synthetic.gdn_inputs([300, 97], 2, 4, 128, 128, seed=45).to("cuda")
     S1, o1 = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
     S2, o2 = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
@@ -165,7 +176,7 @@ def test_deterministic_and_state_only_and_in_place():
     assert torch.equal(buf, ref)
 
 
-def test_beta_zero_is_pure_decay_on_gpu():
+def test_beta_zero_is_pure_decay_on_gpu(schedule):
     # beta = 0: S_m = e^{sum g} S_a and o_t = e^{gamma_t} S_a q_t, checked against the closed form
     inp = synthetic.gdn_inputs([150], 1, 2, 128, 128, seed=46)
     inp.beta.zero_()
@@ -181,7 +192,7 @@ def test_beta_zero_is_pure_decay_on_gpu():
         assert rel(np64(o[:, h]), expect) < OUT_TOL
 
 
-def test_split_call_matches_single_call():
+def test_split_call_matches_single_call(schedule):
     inp = synthetic.gdn_inputs([333], 2, 2, 128, 128, seed=47).to("cuda")
     S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens)
     p = 100
@@ -193,3 +204,58 @@ def test_split_call_matches_single_call():
     for h in range(2):
         assert rel(np64(S2[0, h]), np64(S[0, h])) < STATE_TOL
         assert rel(np64(torch.cat([o1, o2])[:, h]), np64(o[:, h])) < OUT_TOL
+
+
+def _with_schedule(name, fn):
+    prev = get_gdn_schedule()
+    set_gdn_schedule(name)
+    try:
+        return fn()
+    finally:
+        set_gdn_schedule(prev)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_split_schedule_states_equal_fused_bitwise(dk, dv):
+    # Both schedules form the same operands (the split one stores them between its two kernels
+    # and reloads them unchanged) and take the same MFMA steps for the state, so the states
+    # agree bit for bit.  The outputs are formed with the operands swapped in the split scan
+    # (one token per lane for wide stores), a different rounding order: compared within 1e-5.
+    lens = [130, 0, 64, 1, 77]
+    inp = synthetic.gdn_inputs(lens, 2, 4, dk, dv, seed=60 + dk + dv).to("cuda")
+    s_in = torch.randn((len(lens), 4, dv, dk), generator=torch.Generator().manual_seed(8)).cuda() * 0.3
+    run = lambda: gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, q_scale=0.7,  # noqa: E731
+                             state_in=s_in)
+    S_f, o_f = _with_schedule("fused", run)
+    S_s, o_s = _with_schedule("split", run)
+    torch.cuda.synchronize()
+    print("split vs fused: state max |diff| %.3e, output rel %.3e"
+          % ((S_f - S_s).abs().max().item(), rel(np64(o_s), np64(o_f))), flush=True)
+    assert torch.equal(S_f, S_s)
+    assert rel(np64(o_s), np64(o_f)) <= 1e-5
+
+
+def test_split_schedule_empty_sequences_and_workspace_reuse():
+    # every sequence empty: the state passes through; then a larger request reuses a workspace
+    inp = synthetic.gdn_inputs([0, 0], 1, 2, 128, 128, seed=61).to("cuda")
+    s_in = torch.randn((2, 2, 128, 128), generator=torch.Generator().manual_seed(9)).cuda()
+    S, o = _with_schedule("split", lambda: gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                                                      state_in=s_in))
+    torch.cuda.synchronize()
+    assert torch.equal(S, s_in) and o.numel() == 0
+    from linear_attention_state_amd import gdn_replay_workspace_size
+    big = synthetic.gdn_inputs([700, 5], 2, 4, 128, 128, seed=62)
+    prev = get_gdn_schedule()
+    set_gdn_schedule("split")
+    try:
+        n = gdn_replay_workspace_size(big.cu_seqlens, 2, 4, 128, 128, torch.bfloat16)
+        ws = torch.full((n + 4096,), 0xAB, dtype=torch.uint8, device="cuda")   # stale contents
+        small = synthetic.gdn_inputs([64], 2, 4, 128, 128, seed=63)
+        for x in (big, small, big):
+            run_and_compare(x, label="split reuse")
+            d = x.to("cuda")
+            S1, o1 = gdn_replay(d.q, d.k, d.v, d.g, d.beta, x.cu_seqlens, workspace=ws)
+            S2, o2 = gdn_replay(d.q, d.k, d.v, d.g, d.beta, x.cu_seqlens)
+            assert torch.equal(S1, S2) and torch.equal(o1, o2)
+    finally:
+        set_gdn_schedule(prev)
