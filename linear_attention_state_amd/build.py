@@ -36,9 +36,15 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", IN
                 "-Wno-unused-result", "-ffp-contract=fast"]
 
 
+# Per-source flags.  The split scan runs one wave per SIMD, so the register allocator would
+# put its MFMA accumulators in AGPRs and copy the state and outputs to arch VGPRs and back
+# around every elementwise step; this keeps the accumulators in arch VGPRs (167 of them).
+SOURCE_FLAGS = {"gdn_scan_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + COMMON_FLAGS + ["-c", src, "-o", obj]
+    cmd = [_hipcc()] + COMMON_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

@@ -223,7 +223,7 @@ tr_status check_gdn(const char* fn, const int32_t* cu_seqlens_host, const int32_
 // automatically when the fused one would leave most of the chip idle: at most
 // kSplitMaxWaves state-scan waves (32 value columns each).
 std::atomic<int> g_schedule{TR_SCHEDULE_AUTO};
-constexpr int64_t kSplitMaxWaves = 256;
+constexpr int64_t kSplitMaxWaves = 512;
 
 bool use_split(int32_t B, int32_t Hv, int32_t dv, tr_dtype dt) {
     if (dt != TR_BF16) return false;

@@ -18,7 +18,8 @@
 // Data movement: each chunk's fragments go straight from memory to LDS (buffer_load ...
 // lds), two stages deep, so chunk c + 1 lands while chunk c computes.  Each wave issues an
 // equal share of the stage's 1 KiB pieces and waits for its own; a barrier then publishes
-// the stage.  Every LDS read is one lane's 16 bytes of a fragment (conflict-free, and a
+// the stage, and the first pass's fragments of the next chunk are read into registers
+// before the loop turns.  Every LDS read is one lane's 16 bytes of a fragment (conflict-free, and a
 // plain read: the compiler can then tell that the next stage's loads do not touch the
 // stage being read, and adds no wait for them).
 #include "internal.h"
@@ -106,7 +107,7 @@ struct Pieces {
 // time.
 template <int DK, int DV, int NWB, bool WITH_O, int W>
 __device__ __forceinline__ void issue_pieces(Stage<DK, NWB>& S, __amdgpu_buffer_rsrc_t rr, uint32_t rec_soff,
-                                             uint32_t u0_base, int lane) {
+                                             uint32_t u0_base, uint32_t lane16) {
     using PC = Pieces<DK, NWB, WITH_O>;
 #pragma unroll
     for (int p = W; p < PC::TOTAL; p += NWB) {
@@ -124,7 +125,7 @@ __device__ __forceinline__ void issue_pieces(Stage<DK, NWB>& S, __amdgpu_buffer_
         } else {
             dst = reinterpret_cast<bf16*>(&S.tab[0][0]); off = (uint32_t)split_tab_off(DK, DV);
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr)dst, 16, off + lane * 16, rec_soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr)dst, 16, lane16, rec_soff + off, 0, 0);
     }
 }
 
@@ -174,10 +175,11 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
     auto issue_stage = [&](int c, int sidx) {
         const uint32_t rec_soff = (uint32_t)c * REC;
         Stage<DK, NWB>& S = st[sidx];
-        if (wave == 0) issue_pieces<DK, DV, NWB, WITH_O, 0>(S, rr, rec_soff, u0_base, lane);
-        else if (NWB > 1 && wave == 1) issue_pieces<DK, DV, NWB, WITH_O, 1>(S, rr, rec_soff, u0_base, lane);
-        else if (NWB > 2 && wave == 2) issue_pieces<DK, DV, NWB, WITH_O, 2>(S, rr, rec_soff, u0_base, lane);
-        else if (NWB > 3) issue_pieces<DK, DV, NWB, WITH_O, 3>(S, rr, rec_soff, u0_base, lane);
+        const uint32_t lane16 = (uint32_t)(threadIdx.x & 63) * 16;
+        if (wave == 0) issue_pieces<DK, DV, NWB, WITH_O, 0>(S, rr, rec_soff, u0_base, lane16);
+        else if (NWB > 1 && wave == 1) issue_pieces<DK, DV, NWB, WITH_O, 1>(S, rr, rec_soff, u0_base, lane16);
+        else if (NWB > 2 && wave == 2) issue_pieces<DK, DV, NWB, WITH_O, 2>(S, rr, rec_soff, u0_base, lane16);
+        else if (NWB > 3) issue_pieces<DK, DV, NWB, WITH_O, 3>(S, rr, rec_soff, u0_base, lane16);
     };
 
     int l32 = lane & 31, h2 = lane >> 5;
@@ -198,19 +200,28 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
         }
     }
 
-    if (n_chunks > 0) issue_stage(0, 0);
+    // The U'/Y pass's fragments (-W, Q) of chunk c are read at the end of iteration c - 1,
+    // after the stage has landed: the reads cannot drift down to their uses across the loop
+    // edge, so the pass's products find their operands in registers.
+    bf16x8 fw[2 * KSTEPS_D], fq[2 * KSTEPS_D];
+    auto read_pass = [&](const Stage<DK, NWB>& S) {
+#pragma unroll
+        for (int f = 0; f < 2 * KSTEPS_D; ++f) {
+            fw[f] = frag(S.Wn, f, lane);
+            if (WITH_O) fq[f] = frag(S.Q, f, lane);
+        }
+    };
+    if (n_chunks > 0) {
+        issue_stage(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (1 < n_chunks) issue_stage(1, 1);
+        read_pass(st[0]);
+    }
     for (int c = 0; c < n_chunks; ++c) {
         asm volatile("" : "+v"(lane));
         l32 = lane & 31; h2 = (lane >> 5) & 1;
         const Stage<DK, NWB>& S = st[c & 1];
-
-        // Wait for this wave's share of chunk c (only the previous chunk's output stores were
-        // issued after it), then for everyone's; the barrier also ends every wave's reads of
-        // the other stage, which the next issue overwrites.
-        if (WITH_O && c > 0) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        if (c + 1 < n_chunks) issue_stage(c + 1, (c + 1) & 1);
 
         // U0 of this wave's columns (accumulator registers as the prep kernel left them)
         f32x16 U[2];
@@ -234,8 +245,8 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
             const bf16x8 sb = acc_to_b(St[s >> 1], s);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                U[rt] = mma32(frag(S.Wn, rt * KSTEPS_D + s, lane), sb, U[rt]);
-                if (WITH_O) Y[rt] = mma32(sb, frag(S.Q, rt * KSTEPS_D + s, lane), Y[rt]);
+                U[rt] = mma32(fw[rt * KSTEPS_D + s], sb, U[rt]);
+                if (WITH_O) Y[rt] = mma32(sb, fq[rt * KSTEPS_D + s], Y[rt]);
             }
         }
         bf16x8 uh[4], ul[4];
@@ -301,6 +312,16 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), ro, ooff + 16 * qq, soff, 0);
                 }
             }
+        }
+        if (c + 1 < n_chunks) {
+            // Wait for this wave's share of chunk c + 1 (only this chunk's output stores were
+            // issued after it), then for everyone's; the barrier also ends every wave's reads of
+            // this chunk's stage, which the issue of chunk c + 2 overwrites.
+            if (WITH_O) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            if (c + 2 < n_chunks) issue_stage(c + 2, c & 1);
+            read_pass(st[(c + 1) & 1]);
         }
     }
 
