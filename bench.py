@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import gc
 import json
+import re
 import os
 import sys
 import time
@@ -35,8 +36,11 @@ KERNEL_SOURCES = {
     "gemm_tn_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
     "rmsnorm_kernel": "linear_attention_state_amd/csrc/la_layer.hip",
     "gdn_chunk_bf16_kernel": "linear_attention_state_amd/csrc/gdn_chunk_bf16.hip",
+    "gdn_scan_split_kernel": "linear_attention_state_amd/csrc/gdn_scan_split.hip",
     "gdn_decode_kernel": "linear_attention_state_amd/csrc/state_ops.hip",
 }
+# the split schedule's two kernels, whose traffic adds up to one tr_gdn_replay call
+SPLIT_KERNELS = ("gdn_chunk_bf16_kernel<{dk},{dv}> prep", "gdn_scan_split_kernel<{dk},{dv}>")
 COPY_BYTES = 1 << 30
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "replayed token-heads/sec (GDN state rebuild)"
@@ -84,6 +88,10 @@ def measured_traffic(kernel_name, workload):
             table = json.load(f)
     except (OSError, ValueError):
         return None
+    m = re.match(r"gdn split schedule <(\d+),(\d+)>", kernel_name)
+    if m:
+        parts = [measured_traffic(k.format(dk=m.group(1), dv=m.group(2)), workload) for k in SPLIT_KERNELS]
+        return None if None in parts else sum(parts)
     key = kernel_name.split(" (")[0] + "@" + workload
     ent = table.get("kernels", {}).get(key)
     if not ent:
@@ -352,7 +360,8 @@ def run_fidelity(args):
     |S_a Phi| / |S_m| (both from the GPU path), and the times."""
     import torch
     import synthetic
-    from linear_attention_state_amd import gdn_replay, gdn_transition, state_compose, tail_seqlens
+    from linear_attention_state_amd import (gdn_replay, gdn_replay_workspace_size, gdn_transition, state_compose,
+                                            tail_seqlens)
     spec = synthetic.WORKLOADS["fidelity"]
     m, H, d = spec["m"], spec["Hv"], spec["dk"]
     inp = synthetic.gdn_inputs([m], spec["Hqk"], H, d, d, seed=args.seed, backend="torch", device="cuda")
@@ -360,8 +369,14 @@ def run_fidelity(args):
     cu_m_dev = cu_m.cuda()
     S_m = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
 
+    def workspace(cu):
+        n = gdn_replay_workspace_size(cu, spec["Hqk"], H, d, d, torch.bfloat16)
+        return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    ws_m = workspace(cu_m)
+
     def full():
-        gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_m, cu_seqlens_dev=cu_m_dev, state_out=S_m, want_o=False)
+        gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_m, cu_seqlens_dev=cu_m_dev, state_out=S_m, want_o=False,
+                   workspace=ws_m)
     t_full = time_launches(full, max(args.steps, 5), 1)[0]
     res = {}
     for rn, rd in spec["rs"]:
@@ -372,9 +387,10 @@ def run_fidelity(args):
         cu_k = torch.tensor([0, k], dtype=torch.int32)
         cu_k_dev = cu_k.cuda()
         S_hat = torch.empty_like(S_m)
+        ws_k = workspace(cu_k)
 
         def replay():
-            gdn_replay(*tail, cu_k, cu_seqlens_dev=cu_k_dev, state_out=S_hat, want_o=False)
+            gdn_replay(*tail, cu_k, cu_seqlens_dev=cu_k_dev, state_out=S_hat, want_o=False, workspace=ws_k)
         t_rep = time_launches(replay, max(args.steps, 5), 1)[0]
         psi = torch.empty_like(S_m)
 
@@ -395,8 +411,10 @@ def run_fidelity(args):
             rel_state_error_max=float(measured.max()), rel_state_error_mean=float(measured.mean()),
             log10_exact_truncation_max=float(log10_exact.max()))
     nbytes = gdn_bytes(m, 1, spec["Hqk"], H, d, d, with_o=False)
+    kname = ("gdn split schedule <128,128> (state only, one 32768-token sequence)" if ws_m is not None
+             else "gdn_chunk_bf16_kernel<128,128> (state only, one 32768-token sequence)")
     roof = dict(bound="hbm", achieved=nbytes / (t_full * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
-                traffic=None, kernel="gdn_chunk_bf16_kernel<128,128> (state only, one 32768-token sequence)",
+                traffic=None, kernel=kname,
                 algorithmic_bytes=nbytes, avg_launch_us=t_full * 1e3)
     roof["frac"] = roof["achieved"] / roof["peak"]
     config = dict(workload="fidelity", tokens=m, Hqk=spec["Hqk"], Hv=H, dk=d, dv=d, chunk=64,
