@@ -299,7 +299,26 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     a.log_scale_out = nullptr;
     a.uniform_len = 0; a.state_bstride = (int64_t)Hv * dv * dk;
     hipStream_t s = (hipStream_t)stream;
-    if (!split) return finish_launch(launch_gdn(a, dt, s), s, fn);
+    if (!split) {
+        // Fused schedule: with unequal lengths, the longest sequences go first so that they do
+        // not start in the last round of workgroups.
+        if (dt == TR_BF16 && B > 1 && B <= tr::kMaxOrdered) {
+            bool uniform = true;
+            for (int32_t b = 1; b < B && uniform; ++b)
+                uniform = cu_seqlens_host[b + 1] - cu_seqlens_host[b] == cu_seqlens_host[1] - cu_seqlens_host[0];
+            if (!uniform) {
+                std::vector<int32_t> idx(B);
+                for (int32_t b = 0; b < B; ++b) idx[b] = b;
+                std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+                    return cu_seqlens_host[x + 1] - cu_seqlens_host[x] > cu_seqlens_host[y + 1] - cu_seqlens_host[y];
+                });
+                tr::SeqOrder order{};
+                for (int32_t r = 0; r < B; ++r) order.idx[r] = (uint16_t)idx[r];
+                return finish_launch(tr::launch_gdn_chunk_bf16(a, s, &order), s, fn);
+            }
+        }
+        return finish_launch(launch_gdn(a, dt, s), s, fn);
+    }
     // split schedule: chunk-parallel prep into the workspace, then the state scan split along dv
     tr::SplitPlan plan;
     plan.ws = workspace;

@@ -201,9 +201,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // WITH_O: per-token outputs are produced (Q is loaded, Q K^T and P formed, O stored); without
 // them the kernel is the state-only scan.
+// Sequence at longest-first rank `rank`: the order travels as the kernel's first argument and
+// is read through the kernel-argument segment (indexing the by-value argument with a variable
+// would copy it to scratch memory).
+__device__ __forceinline__ int seq_at(int rank) {
+    typedef const __attribute__((address_space(4))) uint16_t kshort;
+    return ((kshort*)__builtin_amdgcn_kernarg_segment_ptr())[rank];
+}
+
 template <int DK, int DV, bool WITH_O, bool PREP>
 __global__ void __launch_bounds__(DV * 2, 2)
-gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict__ q, const bf16* __restrict__ k,
                       const bf16* __restrict__ v, const float* __restrict__ g,
                       const float* __restrict__ beta, const int32_t* __restrict__ cu,
                       int B, int Hqk, int Hv, float q_scale, int uniform_len, long long state_bstride,
@@ -238,16 +246,28 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     int tr_p = (lane & 15) >> 2;
     int tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // Workgroup order: consecutive work items (the value heads that share a query/key head
-    // come next to each other) go to one XCD (blockIdx % 8 picks the XCD), so the second
-    // reader of each key/query tile finds it in that XCD's L2.
-    const int per_xcd = (int)(gridDim.x / 8);
-    const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    // PREP items are (sequence, chunk, value head), value head fastest
-    if (item >= B * Hv * (PREP ? cmax : 1)) return;
-    const int b = PREP ? item / (Hv * cmax) : item / Hv;
-    const int hv = item % Hv;
-    const int hq = hv / (Hv / Hqk);
+    // Workgroup order.  blockIdx % 8 picks the XCD.  Fused: units (sequence, query/key head)
+    // are dealt round-robin to the XCDs in rank order (sequences longest first when ordered),
+    // and the value heads of a unit follow one another on its XCD, so the second reader of
+    // each key/query tile finds it in that XCD's L2.  PREP: items (sequence, chunk, value
+    // head) in contiguous ranges per XCD, value head fastest.
+    const int G = Hv / Hqk;
+    int b, hv, item = 0;
+    if (PREP) {
+        const int per_xcd = (int)(gridDim.x / 8);
+        item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+        if (item >= B * Hv * cmax) return;
+        b = item / (Hv * cmax);
+        hv = item % Hv;
+    } else {
+        const int r = (int)(blockIdx.x / 8);
+        const int u = (r / G) * 8 + (int)(blockIdx.x % 8);
+        if (u >= B * Hqk) return;
+        b = ordered ? seq_at(u / Hqk) : u / Hqk;
+        hv = (u % Hqk) * G + r % G;
+    }
+    (void)order;
+    const int hq = hv / G;
     const int bos = cu ? cu[b] : b * uniform_len;
     const int len = cu ? cu[b + 1] - bos : uniform_len;
     const int n_chunks = (len + CH - 1) / CH;
@@ -764,15 +784,20 @@ gdn_chunk_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 }
 
 template <int DK, int DV, bool WITH_O, bool PREP>
-hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
+hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, const SeqOrder* order, hipStream_t stream) {
     auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O, PREP>;
     const size_t smem = sizeof(Smem<DK, DV>);
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    const long long items = (long long)a.B * a.Hv * (PREP ? plan->cmax : 1);
-    const dim3 grid((unsigned)((items + 7) / 8 * 8));    // a multiple of 8: one share per XCD
+    // a multiple of 8 blocks (one share per XCD); fused: ceil(units / 8) rounds of 8 units
+    const long long units = (long long)a.B * a.Hqk;
+    const long long blocks = PREP ? ((long long)a.B * a.Hv * plan->cmax + 7) / 8 * 8
+                                  : (units + 7) / 8 * 8 * (a.Hv / a.Hqk);
+    const dim3 grid((unsigned)blocks);
     const dim3 block(DV * 2);
-    hipLaunchKernelGGL(kern, grid, block, smem, stream,
+    SeqOrder ord{};
+    if (order) ord = *order;
+    hipLaunchKernelGGL(kern, grid, block, smem, stream, ord, order ? 1 : 0,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
                        a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
                        a.state_in, a.state_identity, a.state_out, (bf16*)a.o,
@@ -782,28 +807,28 @@ hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, hipStream_t s
 }
 
 template <int DK, int DV, bool PREP>
-hipError_t launch(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
-    return a.o ? launch_variant<DK, DV, true, PREP>(a, plan, stream)
-               : launch_variant<DK, DV, false, PREP>(a, plan, stream);
+hipError_t launch(const GdnArgs& a, const SplitPlan* plan, const SeqOrder* order, hipStream_t stream) {
+    return a.o ? launch_variant<DK, DV, true, PREP>(a, plan, order, stream)
+               : launch_variant<DK, DV, false, PREP>(a, plan, order, stream);
 }
 
 template <bool PREP>
-hipError_t launch_dims(const GdnArgs& a, const SplitPlan* plan, hipStream_t stream) {
-    if (a.dk == 128 && a.dv == 128) return launch<128, 128, PREP>(a, plan, stream);
-    if (a.dk == 64 && a.dv == 64) return launch<64, 64, PREP>(a, plan, stream);
-    if (a.dk == 128 && a.dv == 64) return launch<128, 64, PREP>(a, plan, stream);
-    if (a.dk == 64 && a.dv == 128) return launch<64, 128, PREP>(a, plan, stream);
+hipError_t launch_dims(const GdnArgs& a, const SplitPlan* plan, const SeqOrder* order, hipStream_t stream) {
+    if (a.dk == 128 && a.dv == 128) return launch<128, 128, PREP>(a, plan, order, stream);
+    if (a.dk == 64 && a.dv == 64) return launch<64, 64, PREP>(a, plan, order, stream);
+    if (a.dk == 128 && a.dv == 64) return launch<128, 64, PREP>(a, plan, order, stream);
+    if (a.dk == 64 && a.dv == 128) return launch<64, 128, PREP>(a, plan, order, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream) {
-    return launch_dims<false>(a, nullptr, stream);
+hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream, const SeqOrder* order) {
+    return launch_dims<false>(a, nullptr, order, stream);
 }
 
 hipError_t launch_gdn_prep_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream) {
-    return launch_dims<true>(a, &plan, stream);
+    return launch_dims<true>(a, &plan, nullptr, stream);
 }
 
 }  // namespace tr

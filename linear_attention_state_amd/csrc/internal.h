@@ -30,7 +30,14 @@ struct GdnArgs {
 };
 
 // Chunked WY-form recurrence, bf16 operands, fp32 state (gdn_chunk_bf16.hip).
-hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream);
+// The fused kernel takes the sequences longest first when the host passes an order (at most
+// kMaxOrdered sequences of unequal lengths): the longest replays then start in the first
+// round of workgroups instead of wherever they fall in the packing.
+constexpr int kMaxOrdered = 256;
+struct SeqOrder {
+    uint16_t idx[kMaxOrdered];   // idx[rank] = sequence
+};
+hipError_t launch_gdn_chunk_bf16(const GdnArgs& a, hipStream_t stream, const SeqOrder* order = nullptr);
 
 // Split schedule for few heads: a chunk-parallel prep kernel writes one record per
 // (value head, chunk) to the workspace, then the state scan runs with each state split
