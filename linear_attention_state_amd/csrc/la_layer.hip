@@ -199,6 +199,10 @@ gemm_tn_kernel(const GemmParams p)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    // A wave whose 128 x 64 block lies wholly past the last row or column (the last row tile
+    // of a group, the gate tile) still loads and meets the barriers but skips its products,
+    // so the live waves of a ragged tile have their SIMDs to themselves.
+    const bool live = mt * BM + wm * TM * 32 < p.M && nt * BN + wn * TN * 32 < p.N;
     const int KT = __builtin_amdgcn_readfirstlane(p.K / BK);
     issue(0);
     for (int kt = 0; kt < KT; ++kt) {
@@ -206,6 +210,7 @@ gemm_tn_kernel(const GemmParams p)
         // passing also means every wave is done reading the slot that slice kt + 1 overwrites
         asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (kt + 1 < KT) issue(kt + 1);
+        if (!live) continue;
         const unsigned char* slot = smem + (kt & 1) * SLOT_BYTES;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
