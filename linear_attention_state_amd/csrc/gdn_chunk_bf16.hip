@@ -398,43 +398,77 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         lds_barrier();
 
         // ------------------------------------------------------------- P1: K K^T -> L
+        // Diagonal tiles come out with lane (n, q) holding rows 4q..4q+3 of column n (the layout
+        // the inverse reads as fp32); off-diagonal tiles are formed transposed (operands
+        // swapped), so lane (m, q) holds row m, columns 4q..4q+3, stored as bf16 rows for the
+        // merges' A operands.
+        auto l_diag = [&](int b, const f32x4& acc) {
+            const int ci = 16 * b + l16;
+            const float gi = sm.g2[ci];
+            const int r0 = 16 * b + 4 * g4;
+            const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
+            f32x4 lv;
 #pragma unroll
-        for (int it = 0; it < G_PER_WAVE; ++it) {
-            const int tt = wave + NW * it;
-            if (tt < 10) {
-                const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-                const int cb = tt - rb * (rb + 1) / 2;
-                // Diagonal tiles come out with lane (n, q) holding rows 4q..4q+3 of column n (the
-                // layout the inverse reads as fp32); off-diagonal tiles are formed transposed
-                // (operands swapped), so lane (m, q) holds row m, columns 4q..4q+3, stored as bf16
-                // rows for the merges' A operands.
-                const bool diag = rb == cb;
-                const bf16* xrow = &sm.K[16 * (diag ? rb : cb) + l16][0];
-                const bf16* krow = &sm.K[16 * (diag ? cb : rb) + l16][0];
-                f32x4 acc = zero4();
+            for (int j = 0; j < 4; ++j)
+                lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
+            *reinterpret_cast<f32x4*>(&sm.lw.l.Ld[b][l16][4 * g4]) = lv;
+        };
+        auto l_off = [&](int rb, int cb, const f32x4& acc) {
+            const int t = 16 * rb + l16;                  // row (later token)
+            const int c0 = 16 * cb + 4 * g4;              // columns c0..c0+3 (earlier tokens)
+            const float gt = sm.g2[t], bt = sm.bt[t];
+            const f32x4 gi = tab4(sm.g2, c0);
+            bf16x4 lv;
 #pragma unroll
-                for (int s = 0; s < DK / 32; ++s)
-                    acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
-                                   *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
-                if (diag) {
-                    const int ci = 16 * cb + l16;
-                    const float gi = sm.g2[ci];
-                    const int r0 = 16 * rb + 4 * g4;
-                    const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
-                    f32x4 lv;
+            for (int j = 0; j < 4; ++j) lv[j] = (bf16)(bt * __builtin_amdgcn_exp2f(gt - gi[j]) * acc[j]);
+            *reinterpret_cast<bf16x4*>(&sm.lw.l.Lb[t][c0]) = lv;
+        };
+        if constexpr (NW == 4) {
+            // Wave w: the diagonal tile (w, w) and two off-diagonal tiles, with no branches so
+            // that the three product chains and their LDS reads overlap:
+            //   w0: (1,0) (2,0)   w1: (2,1) (3,1)   w2: (3,2) (3,0)   w3: (3,0) (3,2) (repeats;
+            // the same values land in the same places).  Tables: 2 bits per block index.
+            constexpr uint32_t R1 = 1 | 2 << 2 | 3 << 4 | 3 << 6, C1 = 0 | 1 << 2 | 2 << 4 | 0 << 6;
+            constexpr uint32_t R2 = 2 | 3 << 2 | 3 << 4 | 3 << 6, C2 = 0 | 1 << 2 | 0 << 4 | 2 << 6;
+            const int r1 = (R1 >> (2 * wave)) & 3, c1 = (C1 >> (2 * wave)) & 3;
+            const int r2 = (R2 >> (2 * wave)) & 3, c2 = (C2 >> (2 * wave)) & 3;
+            const bf16* pd = &sm.K[(16 * wave + l16) & (CH - 1)][8 * g4];
+            const bf16* pa1 = &sm.K[(16 * c1 + l16) & (CH - 1)][8 * g4];
+            const bf16* pb1 = &sm.K[(16 * r1 + l16) & (CH - 1)][8 * g4];
+            const bf16* pa2 = &sm.K[(16 * c2 + l16) & (CH - 1)][8 * g4];
+            const bf16* pb2 = &sm.K[(16 * r2 + l16) & (CH - 1)][8 * g4];
+            f32x4 ad = zero4(), a1 = zero4(), a2 = zero4();
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
-                    *reinterpret_cast<f32x4*>(&sm.lw.l.Ld[rb][l16][4 * g4]) = lv;
-                } else {
-                    const int t = 16 * rb + l16;                  // row (later token)
-                    const int c0 = 16 * cb + 4 * g4;              // columns c0..c0+3 (earlier tokens)
-                    const float gt = sm.g2[t], bt = sm.bt[t];
-                    const f32x4 gi = tab4(sm.g2, c0);
-                    bf16x4 lv;
+            for (int s = 0; s < DK / 32; ++s) {
+                const bf16x8 xd = *reinterpret_cast<const bf16x8*>(pd + 32 * s);
+                const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(pa1 + 32 * s);
+                const bf16x8 y1 = *reinterpret_cast<const bf16x8*>(pb1 + 32 * s);
+                const bf16x8 x2 = *reinterpret_cast<const bf16x8*>(pa2 + 32 * s);
+                const bf16x8 y2 = *reinterpret_cast<const bf16x8*>(pb2 + 32 * s);
+                ad = mma16k32(xd, xd, ad);
+                a1 = mma16k32(x1, y1, a1);
+                a2 = mma16k32(x2, y2, a2);
+            }
+            l_diag(wave, ad);
+            l_off(r1, c1, a1);
+            l_off(r2, c2, a2);
+        } else {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) lv[j] = (bf16)(bt * __builtin_amdgcn_exp2f(gt - gi[j]) * acc[j]);
-                    *reinterpret_cast<bf16x4*>(&sm.lw.l.Lb[t][c0]) = lv;
+            for (int it = 0; it < G_PER_WAVE; ++it) {
+                const int tt = wave + NW * it;
+                if (tt < 10) {
+                    const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+                    const int cb = tt - rb * (rb + 1) / 2;
+                    const bool diag = rb == cb;
+                    const bf16* xrow = &sm.K[16 * (diag ? rb : cb) + l16][0];
+                    const bf16* krow = &sm.K[16 * (diag ? cb : rb) + l16][0];
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < DK / 32; ++s)
+                        acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
+                                       *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
+                    if (diag) l_diag(rb, acc);
+                    else l_off(rb, cb, acc);
                 }
             }
         }
@@ -542,10 +576,12 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                         const bf16* xrow = &sm.Q[16 * rb + l16][0];
                         const bf16* krow = &sm.K[16 * cb + l16][0];
                         f32x4 acc = zero4();
+                        // operands swapped: lane (t, q) ends with row t = 16 rb + t of Q K^T,
+                        // columns 16 cb + 4q .. 16 cb + 4q + 3
 #pragma unroll
                         for (int s = 0; s < DK / 32; ++s)
-                            acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
-                                           *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
+                            acc = mma16k32(*reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4),
+                                           *reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4), acc);
                         tacc[it] = acc;
                     }
                 }
@@ -643,17 +679,19 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                 if (tt < qk_begin(wave + 1)) {
                     const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
                     const int cb = tt - rb * (rb + 1) / 2;
-                    const int ci = 16 * cb + l16;
-                    const float gi = sm.g2[ci];
-                    const int r0 = 16 * rb + 4 * g4;
-                    const f32x4 gt = tab4(sm.g2, r0);
+                    const int t = 16 * rb + l16;
+                    const int c0 = 16 * cb + 4 * g4;
+                    const float gt = sm.g2[t];
+                    const f32x4 gi = tab4(sm.g2, c0);
+                    bf16x4 ph, pl;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p = (ci <= r0 + j) ? q_scale * __builtin_amdgcn_exp2f(gt[j] - gi) * tacc[it][j] : 0.f;
-                        const bf16 ph = (bf16)p;
-                        sm.np.p.Ph[r0 + j][ci] = ph;
-                        sm.np.p.Pl[r0 + j][ci] = (bf16)(p - (float)ph);
+                        const float p = (c0 + j <= t) ? q_scale * __builtin_amdgcn_exp2f(gt - gi[j]) * tacc[it][j] : 0.f;
+                        ph[j] = (bf16)p;
+                        pl[j] = (bf16)(p - (float)ph[j]);
                     }
+                    *reinterpret_cast<bf16x4*>(&sm.np.p.Ph[t][c0]) = ph;
+                    *reinterpret_cast<bf16x4*>(&sm.np.p.Pl[t][c0]) = pl;
                 }
             }
         }
