@@ -50,6 +50,8 @@
 // is permuted the same way on both operands (see kperm()).
 #include "internal.h"
 
+#include <type_traits>
+
 namespace tr {
 namespace {
 
@@ -228,8 +230,11 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
     constexpr int G_PER_WAVE = (10 + NW - 1) / NW;          // K K^T tiles per wave (P1)
     // Q K^T tiles (P2): wave w takes tiles [qk_begin(w), qk_begin(w + 1)); the waves with the
     // longer inverse merge chains (low w) take fewer.
-    constexpr int QK_PER_WAVE = NW == 4 ? 4 : 6;
-    auto qk_begin = [](int w) { return NW == 4 ? w * (w + 1) / 2 : (w == 0 ? 0 : (w == 1 ? 4 : 10)); };
+    // With four waves, wave 0 (the longest inverse merge chain) takes tile 0 and waves 1..3
+    // take three tiles each; each count runs as straight-line code, so no branch splits the
+    // product chains.  Tiles are numbered row by row: (0,0) (1,0) (1,1) (2,0) ...
+    constexpr int QK_PER_WAVE = NW == 4 ? 3 : 6;
+    auto qk_begin = [](int w) { return NW == 4 ? (w == 0 ? 0 : 3 * w - 2) : (w == 0 ? 0 : (w == 1 ? 4 : 10)); };
     constexpr float LOG2E = 1.4426950408889634f;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -237,6 +242,21 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto qk_tile = [&](int it, int& rb, int& cb) {
+        const int tt = qk_begin(wave) + it;
+        rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
+        cb = tt - rb * (rb + 1) / 2;
+    };
+    auto qk_live = [&](int it) { return NW == 4 || qk_begin(wave) + it < qk_begin(wave + 1); };
+    // runs f(std::integral_constant<int, n>) with this wave's tile count n
+    auto with_qk_count = [&](auto&& f) {
+        if constexpr (NW == 4) {
+            if (wave == 0) f(std::integral_constant<int, 1>{});
+            else f(std::integral_constant<int, 3>{});
+        } else {
+            f(std::integral_constant<int, QK_PER_WAVE>{});
+        }
+    };
     int lane = tid & 63;
     int l32 = lane & 31;
     int h2 = lane >> 5;
@@ -566,25 +586,28 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                 }
             }
             if (WITH_O) {
-                // Q K^T lower 16x16 tiles, kept in registers until P4
+                // Q K^T lower 16x16 tiles, kept in registers until P4.  Operands swapped: lane
+                // (t, q) ends with row 16 rb + t of Q K^T, columns 16 cb + 4q .. 16 cb + 4q + 3.
+                with_qk_count([&](auto n_c) {
+                    constexpr int N = decltype(n_c)::value;
+                    const bf16* qrow[N];
+                    const bf16* krow[N];
 #pragma unroll
-                for (int it = 0; it < QK_PER_WAVE; ++it) {
-                    const int tt = qk_begin(wave) + it;
-                    if (tt < qk_begin(wave + 1)) {
-                        const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-                        const int cb = tt - rb * (rb + 1) / 2;
-                        const bf16* xrow = &sm.Q[16 * rb + l16][0];
-                        const bf16* krow = &sm.K[16 * cb + l16][0];
-                        f32x4 acc = zero4();
-                        // operands swapped: lane (t, q) ends with row t = 16 rb + t of Q K^T,
-                        // columns 16 cb + 4q .. 16 cb + 4q + 3
-#pragma unroll
-                        for (int s = 0; s < DK / 32; ++s)
-                            acc = mma16k32(*reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4),
-                                           *reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4), acc);
-                        tacc[it] = acc;
+                    for (int it = 0; it < N; ++it) {
+                        int rb, cb;
+                        qk_tile(it, rb, cb);
+                        qrow[it] = &sm.Q[(16 * rb + l16) & (CH - 1)][8 * g4];
+                        krow[it] = &sm.K[(16 * cb + l16) & (CH - 1)][8 * g4];
+                        tacc[it] = zero4();
                     }
-                }
+#pragma unroll
+                    for (int s = 0; s < DK / 32; ++s)
+#pragma unroll
+                        for (int it = 0; it < N; ++it)
+                            if (qk_live(it))
+                                tacc[it] = mma16k32(*reinterpret_cast<const bf16x8*>(krow[it] + 32 * s),
+                                                    *reinterpret_cast<const bf16x8*>(qrow[it] + 32 * s), tacc[it]);
+                });
             }
         }
         lds_barrier();
@@ -673,39 +696,39 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
 
         // ------------------------------------------------------------ P4: P to LDS
         if (WITH_O) {
+            with_qk_count([&](auto n_c) {
+                constexpr int N = decltype(n_c)::value;
 #pragma unroll
-            for (int it = 0; it < QK_PER_WAVE; ++it) {
-                const int tt = qk_begin(wave) + it;
-                if (tt < qk_begin(wave + 1)) {
-                    const int rb = tt >= 6 ? 3 : (tt >= 3 ? 2 : (tt >= 1 ? 1 : 0));
-                    const int cb = tt - rb * (rb + 1) / 2;
-                    const int t = 16 * rb + l16;
-                    const int c0 = 16 * cb + 4 * g4;
-                    const float gt = sm.g2[t];
-                    const f32x4 gi = tab4(sm.g2, c0);
-                    bf16x4 ph, pl;
+                for (int it = 0; it < N; ++it) {
+                    if (qk_live(it)) {
+                        int rb, cb;
+                        qk_tile(it, rb, cb);
+                        const int t = 16 * rb + l16;
+                        const int c0 = 16 * cb + 4 * g4;
+                        const float gt = sm.g2[t];
+                        const f32x4 gi = tab4(sm.g2, c0);
+                        bf16x4 ph, pl;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p = (c0 + j <= t) ? q_scale * __builtin_amdgcn_exp2f(gt - gi[j]) * tacc[it][j] : 0.f;
-                        ph[j] = (bf16)p;
-                        pl[j] = (bf16)(p - (float)ph[j]);
+                        for (int j = 0; j < 4; ++j) {
+                            const float p = (c0 + j <= t) ? q_scale * __builtin_amdgcn_exp2f(gt - gi[j]) * tacc[it][j] : 0.f;
+                            ph[j] = (bf16)p;
+                            pl[j] = (bf16)(p - (float)ph[j]);
+                        }
+                        *reinterpret_cast<bf16x4*>(&sm.np.p.Ph[t][c0]) = ph;
+                        *reinterpret_cast<bf16x4*>(&sm.np.p.Pl[t][c0]) = pl;
                     }
-                    *reinterpret_cast<bf16x4*>(&sm.np.p.Ph[t][c0]) = ph;
-                    *reinterpret_cast<bf16x4*>(&sm.np.p.Pl[t][c0]) = pl;
                 }
+            });
+            // the zero blocks above the diagonal inside each 32-row band (also zero for A - I):
+            // (band, hi / lo) = (w & 1, w >> 1) for wave w when there are four waves
+#pragma unroll
+            for (int z = 0; z < 4 / NW; ++z) {
+                const int zb = NW == 4 ? wave : 2 * wave + z;
+                const int band = zb & 1;
+                bf16* zp = (zb >> 1) ? &sm.np.p.Pl[32 * band + l16][32 * band + 16 + 4 * g4]
+                                     : &sm.np.p.Ph[32 * band + l16][32 * band + 16 + 4 * g4];
+                *reinterpret_cast<bf16x4*>(zp) = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
             }
-        }
-        if (WITH_O && wave == 0) {
-            // the zero blocks above the diagonal inside each 32-row band (also zero for A - I)
-#pragma unroll
-            for (int band = 0; band < 2; ++band)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rt = 32 * band + 4 * g4 + j;
-                    const int ci = 32 * band + 16 + l16;
-                    sm.np.p.Ph[rt][ci] = (bf16)0.f;
-                    sm.np.p.Pl[rt][ci] = (bf16)0.f;
-                }
         }
         lds_barrier();
 
