@@ -362,19 +362,10 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
             pb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (uint32_t)lane * gb_stride, soff, 0));
         }
     };
-    if (c_begin < c_end) fetch_kq(c_begin);
-
-    for (int c = c_begin; c < c_end; ++c) {
-        // Recompute the lane-derived indices every chunk: left loop-invariant, the compiler
-        // hoists dozens of per-lane LDS addresses out of the loop and spills them.
-        asm volatile("" : "+v"(lane));
-        l32 = lane & 31; h2 = lane >> 5; l16 = lane & 15; g4 = lane >> 4;
-        tr_p = (lane & 15) >> 2; tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        kq_row = (64 * wave + lane) / TPR; kq_col = ((64 * wave + lane) % TPR) * 8;
-        const int t0 = bos + c * CH;
-        const int nval = min(CH, len - c * CH);
-
-        // -------------------------------------------------------------- P0: stage
+    // The first chunk's K and tables are also staged here (the top of the loop stages them once
+    // more): with its loads consumed before the loop, the compiler's wait at the top of the loop
+    // is for the prefetch alone, not for the previous chunk's output stores issued after it.
+    auto stage = [&]() {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p)
             *reinterpret_cast<bf16x8*>(&sm.K[kq_row + RPP * p][kq_col]) = pk[p];
@@ -389,6 +380,24 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
             sm.qeg[lane] = q_scale * e;
             sm.dec[lane] = __builtin_amdgcn_exp2f(g2_last - g2);
         }
+    };
+    if (c_begin < c_end) {
+        fetch_kq(c_begin);
+        stage();
+    }
+
+    for (int c = c_begin; c < c_end; ++c) {
+        // Recompute the lane-derived indices every chunk: left loop-invariant, the compiler
+        // hoists dozens of per-lane LDS addresses out of the loop and spills them.
+        asm volatile("" : "+v"(lane));
+        l32 = lane & 31; h2 = lane >> 5; l16 = lane & 15; g4 = lane >> 4;
+        tr_p = (lane & 15) >> 2; tr_c = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        kq_row = (64 * wave + lane) / TPR; kq_col = ((64 * wave + lane) % TPR) * 8;
+        const int t0 = bos + c * CH;
+        const int nval = min(CH, len - c * CH);
+
+        // -------------------------------------------------------------- P0: stage
+        stage();
         // This chunk's Q and V are issued after the tables: the gate values reloaded above
         // must not queue behind them.
         if (WITH_O) {
