@@ -60,6 +60,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -826,14 +827,20 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
             }
         }
         if (WITH_O) {
-            const uint32_t ooff = (uint32_t)(4 * h2) * v_stride + (uint32_t)(col0 + l32) * 2;
+            // O as 32-bit words: for each token pair (t, t + 1) a lane holds, lanes 2m and 2m + 1
+            // swap halves and store columns (2m, 2m + 1) of tokens t and t + 1 respectively
+            // (half the store instructions of 16-bit stores, the same cache lines).
+            const uint32_t ooff = (uint32_t)(4 * h2 + (l32 & 1)) * v_stride + (uint32_t)(col0 + (l32 & ~1)) * 2;
+            const uint32_t sel = (l32 & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
+                for (int j = 0; j < 16; j += 2) {
+                    const uint32_t own = __builtin_bit_cast(uint32_t, bf16x2{(bf16)Y[rt][j], (bf16)Y[rt][j + 1]});
+                    const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+                    const uint32_t wv = __builtin_amdgcn_perm(partner, own, sel);
                     const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
-                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)Y[rt][j]), ro,
-                                                          ooff, soff, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(wv, ro, ooff, soff, 0);
                 }
         }
         lds_barrier();
