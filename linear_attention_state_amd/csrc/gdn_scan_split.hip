@@ -31,7 +31,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -141,9 +141,10 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
     constexpr int KSTEPS_D = DK / 16;
     constexpr uint32_t REC = (uint32_t)split_record_bytes(DK, DV);
     // each wave's memory operations between its wait for a stage and the wait before it:
-    // its pieces of the next stage and its output stores (8)
+    // its pieces of the next stage and its output stores
     constexpr int OWN_PIECES = (PC::TOTAL + NWB - 1) / NWB;
-    static_assert(OWN_PIECES + 8 <= 63, "more memory operations in flight than vmcnt counts");
+    constexpr int O_STORES = WITH_O ? 16 : 0;
+    static_assert(OWN_PIECES + O_STORES <= 63, "more memory operations in flight than vmcnt counts");
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Stage<DK, NWB>* st = reinterpret_cast<Stage<DK, NWB>*>(smem_raw);
@@ -234,7 +235,7 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                 for (int i = 0; i < 4; ++i) U[rt][4 * q4 + i] = x[i];
             }
 
-        // U' = U0 + (-W) S^T and Y^T = S Q^T in one pass over the state operands
+        // U' = U0 + (-W) S^T and Y = Q S^T in one pass over the state operands
         f32x16 Y[2];
         if (WITH_O) {
             Y[0] = zero16();
@@ -246,7 +247,7 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 U[rt] = mma32(fw[rt * KSTEPS_D + s], sb, U[rt]);
-                if (WITH_O) Y[rt] = mma32(sb, fq[rt * KSTEPS_D + s], Y[rt]);
+                if (WITH_O) Y[rt] = mma32(fq[rt * KSTEPS_D + s], sb, Y[rt]);
             }
         }
         bf16x8 uh[4], ul[4];
@@ -254,13 +255,15 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, uh[s], ul[s]);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const float e = S.tab[1][32 * rt + l32];     // one token per lane in Y^T
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) Y[rt][i] *= e;
-            }
+                for (int j4 = 0; j4 < 4; ++j4) {
+                    const f32x4 e = *reinterpret_cast<const f32x4*>(&S.tab[1][32 * rt + 8 * j4 + 4 * h2]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Y[rt][4 * j4 + i] *= e[i];
+                }
         }
-        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K and (P U')^T = U'^T P^T
+        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K and O = Y + P U'
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -291,34 +294,36 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                         const int f = rt == 0 ? s : 2 + s;
                         const bf16x8 ph = frag(S.Ph, f, lane);
                         const bf16x8 pl = frag(S.Pl, f, lane);
-                        Y[rt] = mma32(uh[s], ph, Y[rt]);
-                        Y[rt] = mma32(ul[s], ph, Y[rt]);
-                        Y[rt] = mma32(uh[s], pl, Y[rt]);
+                        Y[rt] = mma32(ph, uh[s], Y[rt]);
+                        Y[rt] = mma32(ph, ul[s], Y[rt]);
+                        Y[rt] = mma32(pl, uh[s], Y[rt]);
                     }
                 }
             }
         }
         if (WITH_O) {
-            // O^T: lane (t, h) holds token 32 rt + t, value columns col0 + 8 q + 4 h + {0..3}
-            const uint32_t soff = (uint32_t)(c * CH) * v_stride;
+            // O as 32-bit words: lane (l, h) holds column col0 + l of tokens 8 q + 4 h + {0..3}
+            // (per row tile); for each token pair (t, t + 1), lanes 2m and 2m + 1 swap halves and
+            // store columns (2m, 2m + 1) of tokens t and t + 1 respectively, so each store
+            // instruction covers whole 64-byte row runs.
+            const uint32_t ooff = (uint32_t)(4 * h2 + (l32 & 1)) * v_stride + (uint32_t)(col0 + (l32 & ~1)) * 2;
+            const uint32_t sel = (l32 & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const uint32_t ooff = (uint32_t)(32 * rt + l32) * v_stride + (uint32_t)(col0 + 4 * h2) * 2;
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    bf16x4 ov;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)Y[rt][4 * qq + e];
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ov), ro, ooff + 16 * qq, soff, 0);
+                for (int j = 0; j < 16; j += 2) {
+                    const uint32_t own = __builtin_bit_cast(uint32_t, bf16x2{(bf16)Y[rt][j], (bf16)Y[rt][j + 1]});
+                    const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+                    const uint32_t wv = __builtin_amdgcn_perm(partner, own, sel);
+                    const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
+                    __builtin_amdgcn_raw_buffer_store_b32(wv, ro, ooff, soff, 0);
                 }
-            }
         }
         if (c + 1 < n_chunks) {
             // Wait for this wave's share of chunk c + 1 (only this chunk's output stores were
             // issued after it), then for everyone's; the barrier also ends every wave's reads of
             // this chunk's stage, which the issue of chunk c + 2 overwrites.
-            if (WITH_O) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" :: "i"(O_STORES) : "memory");
             __builtin_amdgcn_s_barrier();
             if (c + 2 < n_chunks) issue_stage(c + 2, c & 1);
             read_pass(st[(c + 1) & 1]);
