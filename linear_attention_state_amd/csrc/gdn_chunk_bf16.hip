@@ -36,9 +36,9 @@
 //   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
 //       K^T operands come from the row-major K tile through LDS transpose reads
 //   P4  P (bf16 hi/lo) to LDS, over the dead (A - I) tiles
-//   P5  U' = U0 + (-W) S^T and Y = Q S^T in one pass over the state operands; then the state
-//       update S <- e^{gamma_n} S + U'^T D K and O = e^gamma q_scale Y + P U' share the
-//       token k-steps (independent accumulators); O stored
+//   P5  U' = U0 + (-W) S^T and Y = Q S^T in one pass over the state operands; then
+//       O = e^gamma q_scale Y + P U', stored, and after it the state update
+//       S <- e^{gamma_n} S + U'^T D K (the output accumulators are free by then)
 // The state-only variant (WITH_O = false) drops Q, Q K^T, P and O.
 //
 // PREP = true is the first kernel of the split schedule (few heads): one workgroup per
@@ -772,9 +772,10 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                 if (WITH_O) Y[rt] = mma32(kperm(&sm.Q[32 * rt + l32][0], s, h2), sb, Y[rt]);
             }
         }
-        // U' as the B operand of P U' (hi/lo split), before the decay scaling below
-        bf16x8 uh[4], ul[4];
+        // Outputs first: O = diag(q_scale e^gamma) Y + P U' (P and U' split hi / lo), stored before
+        // the state update so that its accumulators are free during the update.
         if (WITH_O) {
+            bf16x8 uh[4], ul[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) acc_to_b_split(U[s >> 1], s, uh[s], ul[s]);
 #pragma unroll
@@ -785,10 +786,35 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Y[rt][4 * j4 + i] *= e[i];
                 }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    if (s < 2 * rt + 2) {                  // P is lower triangular
+                        const bf16x8 ph = kperm(&sm.np.p.Ph[32 * rt + l32][0], s, h2);
+                        const bf16x8 pl = kperm(&sm.np.p.Pl[32 * rt + l32][0], s, h2);
+                        Y[rt] = mma32(ph, uh[s], Y[rt]);
+                        Y[rt] = mma32(ph, ul[s], Y[rt]);
+                        Y[rt] = mma32(pl, uh[s], Y[rt]);
+                    }
+                }
+            // O as 32-bit words: for each token pair (t, t + 1) a lane holds, lanes 2m and 2m + 1
+            // swap halves and store columns (2m, 2m + 1) of tokens t and t + 1 respectively
+            // (half the store instructions of 16-bit stores, the same cache lines).
+            const uint32_t ooff = (uint32_t)(4 * h2 + (l32 & 1)) * v_stride + (uint32_t)(col0 + (l32 & ~1)) * 2;
+            const uint32_t sel = (l32 & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int j = 0; j < 16; j += 2) {
+                    const uint32_t own = __builtin_bit_cast(uint32_t, bf16x2{(bf16)Y[rt][j], (bf16)Y[rt][j + 1]});
+                    const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+                    const uint32_t wv = __builtin_amdgcn_perm(partner, own, sel);
+                    const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
+                    __builtin_amdgcn_raw_buffer_store_b32(wv, ro, ooff, soff, 0);
+                }
         }
-        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K, and with outputs
-        // O = diag(q_scale e^gamma) Y + P U' in the same token k-steps: the two products use
-        // independent accumulators, so their MFMAs interleave.
+        // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K (U' split hi / lo)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -813,35 +839,6 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                 St[r] = mma32(a, dh, St[r]);
                 St[r] = mma32(a, dl, St[r]);
             }
-            if (WITH_O) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    if (s < 2 * rt + 2) {                  // P is lower triangular
-                        const bf16x8 ph = kperm(&sm.np.p.Ph[32 * rt + l32][0], s, h2);
-                        const bf16x8 pl = kperm(&sm.np.p.Pl[32 * rt + l32][0], s, h2);
-                        Y[rt] = mma32(ph, uh[s], Y[rt]);
-                        Y[rt] = mma32(ph, ul[s], Y[rt]);
-                        Y[rt] = mma32(pl, uh[s], Y[rt]);
-                    }
-                }
-            }
-        }
-        if (WITH_O) {
-            // O as 32-bit words: for each token pair (t, t + 1) a lane holds, lanes 2m and 2m + 1
-            // swap halves and store columns (2m, 2m + 1) of tokens t and t + 1 respectively
-            // (half the store instructions of 16-bit stores, the same cache lines).
-            const uint32_t ooff = (uint32_t)(4 * h2 + (l32 & 1)) * v_stride + (uint32_t)(col0 + (l32 & ~1)) * 2;
-            const uint32_t sel = (l32 & 1) ? 0x03020706u : 0x05040100u;
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int j = 0; j < 16; j += 2) {
-                    const uint32_t own = __builtin_bit_cast(uint32_t, bf16x2{(bf16)Y[rt][j], (bf16)Y[rt][j + 1]});
-                    const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
-                    const uint32_t wv = __builtin_amdgcn_perm(partner, own, sel);
-                    const uint32_t soff = (uint32_t)(c * CH + 32 * rt + 8 * (j >> 2) + (j & 3)) * v_stride;
-                    __builtin_amdgcn_raw_buffer_store_b32(wv, ro, ooff, soff, 0);
-                }
         }
         lds_barrier();
     }
