@@ -564,35 +564,42 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
             // in row order (lane (n, q) holds row n, columns 4q..4q+3), so it is written as
             // 8-byte row segments.  T enters as the A operand in its accumulator layout (which
             // reads as T^T), A_ii as the B operand in row layout (which reads as A_ii^T).
-            auto emit = [&](int i, int j, const bf16x4& tneg) {
-                const f32x4 rows = mma16(tneg, opAd(i), zero4());
+            for (int j = wave; j < 3; j += NW) {
+                // Every operand of block column j's chain is read before the chain starts (block
+                // indices clamped to 3; a clamped operand is never used), so the chain waits
+                // only on its own products.
+                const int j1 = j + 1, j2 = min(j + 2, 3);
+                const bf16x4 dj = opBd(j);
+                const bf16x4 l10 = opL(j1, j), l20 = opL(j2, j), l21 = opL(j2, j1);
+                const bf16x4 l30 = opL(3, j), l31 = opL(3, j1), l32 = opL(3, j2);
+                const bf16x4 d1 = opAd(j1), d2 = opAd(j2), d3 = opAd(3);
                 const int c0 = 16 * j + 4 * g4;
                 const f32x4 bt = tab4(sm.bt, c0), bg = tab4(sm.bg, c0);
-                bf16x4 nb, ng;
+                auto emit = [&](int i, const bf16x4& di, const bf16x4& tneg) {
+                    const f32x4 rows = mma16(tneg, di, zero4());
+                    bf16x4 nb, ng;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nb[e] = (bf16)(rows[e] * bt[e]);
-                    ng[e] = (bf16)(rows[e] * bg[e]);
-                }
-                *reinterpret_cast<bf16x4*>(&sm.np.n.Nb[16 * i + l16][c0]) = nb;
-                *reinterpret_cast<bf16x4*>(&sm.np.n.Nbg[16 * i + l16][c0]) = ng;
-            };
-            for (int j = wave; j < 3; j += NW) {
-                const bf16x4 dj = opBd(j);
-                bf16x4 a1, a2;                        // A_{j+1,j}, A_{j+2,j} as B operands
-                const bf16x4 t1 = to_bf4(mma16(opL(j + 1, j), dj, zero4()), -1.f);
-                if (j + 1 < 3) a1 = to_bf4(mma16(opAd(j + 1), t1, zero4()), 1.f);
-                emit(j + 1, j, t1);
+                    for (int e = 0; e < 4; ++e) {
+                        nb[e] = (bf16)(rows[e] * bt[e]);
+                        ng[e] = (bf16)(rows[e] * bg[e]);
+                    }
+                    *reinterpret_cast<bf16x4*>(&sm.np.n.Nb[16 * i + l16][c0]) = nb;
+                    *reinterpret_cast<bf16x4*>(&sm.np.n.Nbg[16 * i + l16][c0]) = ng;
+                };
+                // A_{j+1,j}, A_{j+2,j} as B operands (a1 unused when j + 1 = 3, a2 unless j = 0)
+                const bf16x4 t1 = to_bf4(mma16(l10, dj, zero4()), -1.f);
+                const bf16x4 a1 = to_bf4(mma16(d1, t1, zero4()), 1.f);
+                emit(j1, d1, t1);
                 if (j + 2 <= 3) {
-                    const bf16x4 t2 = to_bf4(mma16(opL(j + 2, j + 1), a1, mma16(opL(j + 2, j), dj, zero4())), -1.f);
-                    if (j + 2 < 3) a2 = to_bf4(mma16(opAd(j + 2), t2, zero4()), 1.f);
-                    emit(j + 2, j, t2);
-                }
-                if (j + 3 <= 3) {
-                    f32x4 acc = mma16(opL(3, 0), dj, zero4());
-                    acc = mma16(opL(3, 1), a1, acc);
-                    acc = mma16(opL(3, 2), a2, acc);
-                    emit(3, 0, to_bf4(acc, -1.f));
+                    const bf16x4 t2 = to_bf4(mma16(l21, a1, mma16(l20, dj, zero4())), -1.f);
+                    const bf16x4 a2 = to_bf4(mma16(d2, t2, zero4()), 1.f);
+                    emit(j2, d2, t2);
+                    if (j == 0) {
+                        f32x4 acc = mma16(l30, dj, zero4());
+                        acc = mma16(l31, a1, acc);
+                        acc = mma16(l32, a2, acc);
+                        emit(3, d3, to_bf4(acc, -1.f));
+                    }
                 }
             }
             if (WITH_O) {
