@@ -656,6 +656,11 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                             lds_tr4(&sm.K[16 * s + 8 + 4 * h2 + tr_p][32 * ct + tr_c]));
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
+                // the K row segments of the unit-diagonal term, read before the products
+                bf16x4 kt[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    kt[q] = *reinterpret_cast<const bf16x4*>(&sm.K[32 * rt + l32][32 * ct + 8 * q + 4 * h2]);
                 // W^T tile (operands swapped): lane (t = l32, h) holds token 32 rt + t, dk columns
                 // 32 ct + 8 q + 4 h + {0..3} -- 8-byte row segments of -W
                 f32x16 acc = zero16();
@@ -667,10 +672,9 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = 32 * ct + 8 * q + 4 * h2;
-                    const bf16x4 kt = *reinterpret_cast<const bf16x4*>(&sm.K[t][c]);
                     bf16x4 w;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (bf16)(-(acc[4 * q + e] + bgt * (float)kt[e]));
+                    for (int e = 0; e < 4; ++e) w[e] = (bf16)(-(acc[4 * q + e] + bgt * (float)kt[q][e]));
                     *reinterpret_cast<bf16x4*>(&sm.lw.Wn[t][c]) = w;
                 }
             }
