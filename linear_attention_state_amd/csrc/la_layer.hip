@@ -26,7 +26,23 @@ __device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const 
 }
 
 // --------------------------------------------------------------------------- RMSNorm
-// One wave per row of d elements (d % 512 == 0 handled as d / 512 passes of 8 per lane).
+// One wave per row of d elements (d % 8 == 0), 8 per lane per 512-column pass.  A row of up
+// to 512 * RMS_MAXP columns stays in registers between the sum of squares and the scaling, so
+// x is read once; wider rows are read twice.
+constexpr int RMS_MAXP = 8;
+__device__ __forceinline__ bf16x8 rms_scale(const bf16x8& v, const bf16* gr, int c, float r) {
+    bf16x8 o;
+    if (gr) {
+        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gr + c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[i] * r * (float)gv[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[i] * r);
+    }
+    return o;
+}
+
 __global__ void __launch_bounds__(256)
 rmsnorm_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, PtrTable gain, int rows_per_group,
                int rows, int d, float eps)
@@ -35,8 +51,30 @@ rmsnorm_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, PtrTable gain, 
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const bf16* xr = x + (size_t)row * d;
+    bf16* yr = y + (size_t)row * d;
     const bf16* gr = (const bf16*)gain.p[row / rows_per_group];
     float ss = 0.f;
+    if (d <= 512 * RMS_MAXP) {
+        bf16x8 v[RMS_MAXP];
+#pragma unroll
+        for (int p = 0; p < RMS_MAXP; ++p) {
+            const int c = 512 * p + lane * 8;
+            if (c < d) {
+                v[p] = *reinterpret_cast<const bf16x8*>(xr + c);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { const float f = (float)v[p][i]; ss = fmaf(f, f, ss); }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int p = 0; p < RMS_MAXP; ++p) {
+            const int c = 512 * p + lane * 8;
+            if (c < d) *reinterpret_cast<bf16x8*>(yr + c) = rms_scale(v[p], gr, c, r);
+        }
+        return;
+    }
     for (int c = lane * 8; c < d; c += 512) {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c);
 #pragma unroll
@@ -45,20 +83,8 @@ rmsnorm_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, PtrTable gain, 
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    bf16* yr = y + (size_t)row * d;
-    for (int c = lane * 8; c < d; c += 512) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(xr + c);
-        bf16x8 o;
-        if (gr) {
-            const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gr + c);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[i] * r * (float)gv[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[i] * r);
-        }
-        *reinterpret_cast<bf16x8*>(yr + c) = o;
-    }
+    for (int c = lane * 8; c < d; c += 512)
+        *reinterpret_cast<bf16x8*>(yr + c) = rms_scale(*reinterpret_cast<const bf16x8*>(xr + c), gr, c, r);
 }
 
 // --------------------------------------------------------------------------- GEMM

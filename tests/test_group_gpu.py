@@ -18,7 +18,7 @@ import torch
 import oracle
 import synthetic
 from oracle import chain
-from linear_attention_state_amd import GroupReplay, la_layer_inputs, la_output_residual, tail_seqlens
+from linear_attention_state_amd import GroupReplay, la_layer_inputs, la_output_residual, rmsnorm, tail_seqlens
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,25 @@ def weights_np(ws):
 def rel(a, b):
     nb = np.linalg.norm(b)
     return np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
+
+
+@pytest.mark.parametrize("d", [128, 640, 2048, 4096, 4224])
+def test_rmsnorm_widths(d):
+    # rows held in registers up to 4096 columns (including a partial last pass at 640), read
+    # twice beyond; block 0 without a gain, block 1 with one.  The GPU rounds x r gain once to
+    # bf16 from fp32, the oracle from fp64: at most one bf16 ulp apart, rarely.
+    G, n = 2, 37
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(d)
+    x = torch.randn((G, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+    gain = (0.5 + torch.rand(d, generator=gen, device="cuda")).to(torch.bfloat16)
+    y = rmsnorm(x, [None, gain])
+    torch.cuda.synchronize()
+    for b, gb in enumerate([None, gain]):
+        ref = chain.rmsnorm(np64(x[b]), None if gb is None else np64(gb), 1e-6)
+        du = ulp_diff_bf16(np64(y[b]), ref)
+        print("d=%d block %d: max ulp %d, mismatched %.3f%%" % (d, b, du.max(), 100 * np.mean(du > 0)), flush=True)
+        assert du.max() <= 1 and np.mean(du > 0) < 0.01
 
 
 @pytest.mark.parametrize("n,with_gain,Hqk,Hv", [(100, False, 2, 4), (130, True, 2, 4), (77, False, 3, 6)])
