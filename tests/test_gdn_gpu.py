@@ -259,3 +259,30 @@ def test_split_schedule_empty_sequences_and_workspace_reuse():
             assert torch.equal(S1, S2) and torch.equal(o1, o2)
     finally:
         set_gdn_schedule(prev)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_orthonormal_keys_recall_exactly(d, schedule):
+    # alpha = beta = 1 and the keys the standard basis, in a shuffled order: each token
+    # overwrites its own key's column, so the final state holds every value exactly
+    # (S e_j = v_j) and each output reads back its own value (o_t = S_t k_t = v_t).  bf16
+    # keys and values are exact here, and so is every product the chunked form takes.
+    T, Hv = d, 2
+    rng = np.random.default_rng(d)
+    order = rng.permutation(d)
+    keys = np.zeros((T, 1, d), np.float32)
+    keys[np.arange(T), 0, order] = 1.0
+    v = torch.from_numpy(rng.standard_normal((T, Hv, d)).astype(np.float32)).to(torch.bfloat16)
+    kq = torch.from_numpy(keys).to(torch.bfloat16)
+    g = torch.zeros((T, Hv), dtype=torch.float32)
+    beta = torch.ones((T, Hv), dtype=torch.float32)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    S, o = gdn_replay(kq.cuda(), kq.cuda(), v.cuda(), g.cuda(), beta.cuda(), cu)
+    torch.cuda.synchronize()
+    S, o, vf = np64(S), np64(o), np64(v)
+    for h in range(Hv):
+        recalled = S[0, h][:, order].T               # column order[t] of S is v_t
+        print("recall %s d=%d head %d: max |S k - v| %.2e, max |o - v| %.2e"
+              % (schedule, d, h, np.abs(recalled - vf[:, h]).max(), np.abs(o[:, h] - vf[:, h]).max()), flush=True)
+        assert np.abs(recalled - vf[:, h]).max() <= 1e-6 * max(1.0, np.abs(vf).max())
+        np.testing.assert_array_equal(o[:, h], vf[:, h])
