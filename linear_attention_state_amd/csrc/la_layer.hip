@@ -191,7 +191,9 @@ gemm_tn_kernel(const GemmParams p)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, h2 = lane >> 5;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    // Column blocks rotate with the row half (waves w and w + 4 share SIMD w % 4), so the two
+    // live waves of a tile with one live column block (the gate columns) run on two SIMDs.
+    const int wm = wave / WAVES_N, wn = (wave + wm) % WAVES_N;
 
     // Loader: load instruction i of a slot fills slot rows [8i, 8i + 8) (rows 0..255 are A,
     // 256..511 are B); lane l writes bytes [16l, 16l + 16) of its 1 KB, i.e. row l / 8, chunk
@@ -337,11 +339,11 @@ gemm_tn_kernel(const GemmParams p)
     float* ssbuf = reinterpret_cast<float*>(smem + SSBUF_OFFSET);      // [waves][TM][32]
     if (h2 == 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) ssbuf[(wave * TM + i) * 32 + l32] = ss[i];
+        for (int i = 0; i < TM; ++i) ssbuf[((wm * WAVES_N + wn) * TM + i) * 32 + l32] = ss[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ss[i] += ssbuf[((wave ^ 1) * TM + i) * 32 + l32];
+    for (int i = 0; i < TM; ++i) ss[i] += ssbuf[((wm * WAVES_N + (wn ^ 1)) * TM + i) * 32 + l32];
 
     const int seg = 2 * nt + (wn >> 1);
     const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
