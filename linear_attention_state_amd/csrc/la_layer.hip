@@ -18,11 +18,10 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // --------------------------------------------------------------------------- RMSNorm
@@ -88,12 +87,13 @@ rmsnorm_kernel(const bf16* __restrict__ x, bf16* __restrict__ y, PtrTable gain, 
 }
 
 // --------------------------------------------------------------------------- GEMM
-// 256x256 output tile per workgroup of 8 waves (2 x 4 waves of 128x64, 32x32x16 bf16 MFMA).
+// 256x256 output tile per workgroup of 8 waves (2 x 4 waves of 128x64, 16x16x32 bf16 MFMA).
 // The K loop streams 64-wide slices through a 2-slot LDS ring (64 KB per slot) with direct
 // global-to-LDS loads, issued one slice ahead.  Each 128-byte LDS row holds its eight 16-byte
 // chunks in a row-dependent order so that the operand reads hit distinct banks.
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WAVES_N = 4, TM = 4, TN = 2;            // wave grid 2 x 4, wave tile 128 x 64
+constexpr int FM = 2 * TM, FN = 2 * TN;               // 16x16 product tiles per wave: 8 x 4
 constexpr int NTHREADS = 512;
 constexpr int ROW_BYTES = BK * 2;                    // 128
 constexpr int SLOT_BYTES = (BM + BN) * ROW_BYTES;    // A rows then B rows: 64 KB
@@ -190,7 +190,7 @@ gemm_tn_kernel(const GemmParams p)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, h2 = lane >> 5;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     // Column blocks rotate with the row half (waves w and w + 4 share SIMD w % 4), so the two
     // live waves of a tile with one live column block (the gate columns) run on two SIMDs.
     const int wm = wave / WAVES_N, wn = (wave + wm) % WAVES_N;
@@ -219,13 +219,16 @@ gemm_tn_kernel(const GemmParams p)
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + kt * BK), (lds_void*)(slot + 1024 * j), 16, 0, 0);
     };
 
-    f32x16 acc[TM][TN];
+    // acc[i][j] element e of lane (l16, g4) is output row (token) 128 wm + 16 i + l16 and
+    // column 64 wn + 16 j + 4 g4 + e: the operands are swapped, so each lane holds one token
+    // and runs of 4 consecutive output columns.
+    f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
     // A wave whose 128 x 64 block lies wholly past the last row or column (the last row tile
     // of a group, the gate tile) still loads and meets the barriers but skips its products,
@@ -240,47 +243,43 @@ gemm_tn_kernel(const GemmParams p)
         if (kt + 1 < KT) issue(kt + 1);
         if (!live) continue;
         const unsigned char* slot = smem + (kt & 1) * SLOT_BYTES;
+        // two 32-deep k-steps per slice; lane (l16, g4) reads row l16 of each 16-row fragment,
+        // 16-byte chunk 4 ks + g4 (the 16 lanes of one chunk hit distinct banks)
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 af[TM], bfr[TN];
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            bf16x8 af[FM], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * TM * 32 + 32 * i + l32;
-                af[i] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((2 * kk + h2) ^ chunk_swz(r)));
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * TM * 32 + 16 * i + l16;
+                af[i] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((4 * ks + g4) ^ chunk_swz(r)));
             }
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = BM + wn * TN * 32 + 32 * j + l32;
-                bfr[j] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((2 * kk + h2) ^ chunk_swz(r)));
+            for (int j = 0; j < FN; ++j) {
+                const int r = BM + wn * TN * 32 + 16 * j + l16;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(slot + r * ROW_BYTES + 16 * ((4 * ks + g4) ^ chunk_swz(r)));
             }
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                // operands swapped: the accumulator holds the tile transposed, so each lane ends
-                // with one token and runs of 4 consecutive output columns
-                for (int j = 0; j < TN; ++j) acc[i][j] = mma32(bfr[j], af[i], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = mma16(bfr[j], af[i], acc[i][j]);
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- epilogue.  acc[i][j] element e of lane (l32, h2) is output row (token)
-    // 128 wm + 32 i + l32 and column 64 wn + 32 j + 8 (e / 4) + 4 h2 + e % 4.  Each wave turns
-    // its 128 x 64 block around in a private LDS region, then writes whole 128-byte row runs.
+    // ---- epilogue.  Each wave turns its 128 x 64 block around in a private LDS region, then
+    // writes whole 128-byte row runs.
     unsigned char* stg = smem + wave * STG_WAVE_BYTES;
     const int rr = lane >> 3;                 // read-back: row within a group of 8, 16-byte chunk
     const int rc = (lane & 7) * 8;            // first of 8 columns
     if (EPI == EPI_RESIDUAL) {
         float* st = reinterpret_cast<float*>(stg);
-        auto put = [&](const f32x16 (&a)[TN], int ii) {
+        // rows [64 half, 64 half + 64) of the wave's block: product tiles 4 half .. 4 half + 3
+        auto put = [&](int half) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = a[j][4 * q4 + e];
-                    *reinterpret_cast<f32x4*>(st + (32 * ii + l32) * STG_F32_ROW + 32 * j + 8 * q4 + 4 * h2) = x;
-                }
+                for (int j = 0; j < FN; ++j)
+                    *reinterpret_cast<f32x4*>(st + (16 * ii + l16) * STG_F32_ROW + 16 * j + 4 * g4) = acc[4 * half + ii][j];
         };
         // x_in / x_out through buffer views of this wave's rows: rows past M read as zero and
         // their stores are dropped, so the row loop has no branches and the x_in loads can be
@@ -304,7 +303,7 @@ gemm_tn_kernel(const GemmParams p)
                 off[t] = n0 < p.N ? ((uint32_t)row * (uint32_t)p.N + (uint32_t)n0) * 2u : 0xFFFFFFF0u;
                 xv[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rin, off[t], 0, 0));
             }
-            if (half == 0) { put(acc[0], 0); put(acc[1], 1); } else { put(acc[2], 0); put(acc[3], 1); }
+            put(half);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int row = 8 * t + rr;
@@ -326,24 +325,26 @@ gemm_tn_kernel(const GemmParams p)
     // EPI_LAYER_IN.  128-column segments: q heads, k heads, v heads, then one segment of gate
     // logits ([0, Hv) z_a, [Hv, 2 Hv) z_b).  A segment spans waves wn and wn ^ 1; the row sums
     // of squares for the q / k L2 norms meet through LDS.
-    float ss[TM];
+    // row sums of squares: the four lanes (l16, 0..3) of a token hold its 64 columns of this wave
+    float ss[FM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < FM; ++i) {
         float t = 0.f;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) t = fmaf(acc[i][j][e], acc[i][j][e], t);
+            for (int e = 0; e < 4; ++e) t = fmaf(acc[i][j][e], acc[i][j][e], t);
+        t += __shfl_xor(t, 16, 64);
         ss[i] = t + __shfl_xor(t, 32, 64);
     }
-    float* ssbuf = reinterpret_cast<float*>(smem + SSBUF_OFFSET);      // [waves][TM][32]
-    if (h2 == 0) {
+    float* ssbuf = reinterpret_cast<float*>(smem + SSBUF_OFFSET);      // [waves][FM][16]
+    if (g4 == 0) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) ssbuf[((wm * WAVES_N + wn) * TM + i) * 32 + l32] = ss[i];
+        for (int i = 0; i < FM; ++i) ssbuf[((wm * WAVES_N + wn) * FM + i) * 16 + l16] = ss[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ss[i] += ssbuf[((wm * WAVES_N + (wn ^ 1)) * TM + i) * 32 + l32];
+    for (int i = 0; i < FM; ++i) ss[i] += ssbuf[((wm * WAVES_N + (wn ^ 1)) * FM + i) * 16 + l16];
 
     const int seg = 2 * nt + (wn >> 1);
     const int nq = p.Hqk, nk = 2 * p.Hqk, nv = 2 * p.Hqk + p.Hv;
@@ -351,22 +352,17 @@ gemm_tn_kernel(const GemmParams p)
         // q, k (L2-normalised rows, q also scaled) or v: bf16 through the wave's staging rows
         const bool is_qk = seg < nk, is_q = seg < nq;
         bf16* st = reinterpret_cast<bf16*>(stg);
-        auto put = [&](const f32x16 (&a)[TN], float ssi, int i) {
-            const float scale = is_qk ? (is_q ? p.q_scale : 1.f) / sqrtf(ssi + 1e-6f) : 1.f;
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+        for (int i = 0; i < FM; ++i) {
+            const float scale = is_qk ? (is_q ? p.q_scale : 1.f) / sqrtf(ss[i] + 1e-6f) : 1.f;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    bf16x4 ov;
+            for (int j = 0; j < FN; ++j) {
+                bf16x4 ov;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) ov[e] = (bf16)(a[j][4 * q4 + e] * scale);
-                    *reinterpret_cast<bf16x4*>(st + (32 * i + l32) * STG_BF16_ROW + 32 * j + 8 * q4 + 4 * h2) = ov;
-                }
-        };
-        put(acc[0], ss[0], 0);
-        put(acc[1], ss[1], 1);
-        put(acc[2], ss[2], 2);
-        put(acc[3], ss[3], 3);
+                for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[i][j][e] * scale);
+                *reinterpret_cast<bf16x4*>(st + (16 * i + l16) * STG_BF16_ROW + 16 * j + 4 * g4) = ov;
+            }
+        }
         bf16* base = is_qk ? (is_q ? p.q : p.k) : p.v;
         const int heads = is_qk ? p.Hqk : p.Hv;
         const int head = is_qk ? (is_q ? seg : seg - nq) : seg - nk;
@@ -380,42 +376,38 @@ gemm_tn_kernel(const GemmParams p)
         }
     } else if (seg == nv) {
         // gate logits: few columns, written from registers
-        const int cseg = (wn & 1) * TN * 32 + 4 * h2;
-        auto gates = [&](const f32x16 (&a)[TN], int i) {
-            const int m = mt * BM + wm * TM * 32 + 32 * i + l32;
+        const int cseg = (wn & 1) * TN * 32 + 4 * g4;
+        auto gates = [&](const f32x4 (&a)[FN], int i) {
+            const int m = mt * BM + wm * TM * 32 + 16 * i + l16;
             if (m >= p.M) return;
             const size_t grow = (size_t)g * p.M + m;
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < FN; ++j) {
+                const int cg0 = cseg + 16 * j;                      // four consecutive columns
+                if (cg0 >= 2 * p.Hv) continue;
+                if ((p.Hv & 3) == 0) {                              // all four in g or all in beta
+                    const bool is_g = cg0 < p.Hv;
+                    f32x4 r;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int cg0 = cseg + 32 * j + 8 * q4;          // four consecutive columns
-                    if (cg0 >= 2 * p.Hv) continue;
-                    if ((p.Hv & 3) == 0) {                          // all four in g or all in beta
-                        const bool is_g = cg0 < p.Hv;
-                        f32x4 r;
+                    for (int e = 0; e < 4; ++e) {
+                        const float z = a[j][e];
+                        r[e] = is_g ? -softplus_f(z) : sigmoid_f(z);
+                    }
+                    float* dst = is_g ? p.g + grow * p.Hv + cg0 : p.beta + grow * p.Hv + (cg0 - p.Hv);
+                    *reinterpret_cast<f32x4*>(dst) = r;
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float z = a[j][4 * q4 + e];
-                            r[e] = is_g ? -softplus_f(z) : sigmoid_f(z);
-                        }
-                        float* dst = is_g ? p.g + grow * p.Hv + cg0 : p.beta + grow * p.Hv + (cg0 - p.Hv);
-                        *reinterpret_cast<f32x4*>(dst) = r;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int cg = cg0 + e;
-                            const float z = a[j][4 * q4 + e];
-                            if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(z);
-                            else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(z);
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        const int cg = cg0 + e;
+                        const float z = a[j][e];
+                        if (cg < p.Hv) p.g[grow * p.Hv + cg] = -softplus_f(z);
+                        else if (cg < 2 * p.Hv) p.beta[grow * p.Hv + (cg - p.Hv)] = sigmoid_f(z);
                     }
                 }
+            }
         };
-        gates(acc[0], 0);
-        gates(acc[1], 1);
-        gates(acc[2], 2);
-        gates(acc[3], 3);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) gates(acc[i], i);
     }
 }
 
