@@ -534,8 +534,8 @@ def run_overlap(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (the replay shards with no exchange "
-              "step; see the design notes); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only (the replay would shard over heads and hits with no "
+              "exchange step); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

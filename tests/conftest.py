@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so that a plain
-    # `pytest tests/` on a CPU-only host still passes; `-m gpu` on the GPU machine runs them.
+    # `pytest tests/` on a CPU-only host still passes; `-m gpu` on a machine with a GPU runs them.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
