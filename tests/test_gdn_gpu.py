@@ -85,6 +85,14 @@ def test_bf16_ragged_zero_state(dk, dv, schedule):
     run_and_compare(inp, label="bf16 ragged %dx%d %s" % (dk, dv, schedule))
 
 
+@pytest.mark.parametrize("Hqk,Hv", [(1, 4), (3, 3), (2, 8)])
+def test_bf16_ragged_query_key_head_sharing(Hqk, Hv, schedule):
+    # value heads per query/key head G = Hv / Hqk of 4, 1 and 4 (the workgroup order deals
+    # the G value heads of a query/key head to one XCD)
+    inp = synthetic.gdn_inputs(RAGGED, Hqk, Hv, 128, 128, seed=300 + 10 * Hqk + Hv)
+    run_and_compare(inp, label="bf16 heads %d/%d %s" % (Hqk, Hv, schedule))
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
 def test_bf16_ragged_given_state_and_scale(dk, dv, schedule):
     inp = synthetic.gdn_inputs(RAGGED, 1, 3, dk, dv, seed=7 + dk, q_prescaled=False)
