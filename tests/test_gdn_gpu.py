@@ -131,15 +131,16 @@ def _sampled_parity(inp_dev, cu, seqs, heads, Hqk, Hv, S, o):
     return worst_s, worst_o
 
 
-def test_batched_full_size_sampled():
-    # 36 instances x 32 v-heads (16 qk-heads), m = 32768, r = 0.10 -> 3,277 tokens each
-    cu, _ = tail_seqlens([32768] * 36, 10, 100)
+@pytest.mark.parametrize("r_pct", [5, 10])
+def test_batched_full_size_sampled(r_pct):
+    # 36 instances x 32 v-heads (16 qk-heads), m = 32768, r = 0.05 / 0.10 -> 1,639 / 3,277 tokens
+    cu, _ = tail_seqlens([32768] * 36, r_pct, 100)
     inp = synthetic.gdn_inputs(np.diff(cu.numpy()).tolist(), 16, 32, 128, 128, seed=21,
                                backend="torch", device="cuda")
     S, o = gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu)
     torch.cuda.synchronize()
     es, eo = _sampled_parity(inp, cu.numpy(), [0, 17, 35], [0, 1, 30, 31], 16, 32, S, o)
-    print("batched sampled: state %.3e output %.3e" % (es, eo), flush=True)
+    print("batched r = %d%% sampled: state %.3e output %.3e" % (r_pct, es, eo), flush=True)
     assert es <= STATE_TOL and eo <= OUT_TOL
 
 
