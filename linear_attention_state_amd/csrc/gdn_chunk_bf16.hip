@@ -30,9 +30,10 @@
 //       issue this chunk's Q and V loads and the next chunk's K, g, beta loads
 //   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L^T (fp32) in LDS;
 //       stage Q
-//   P2  A = (I + L)^{-1} on wave 0: fp32 back substitution of the four 16x16 diagonal blocks
-//       (a 16-lane group per block, each lane one row), 16x16x16 MFMA merges in registers;
-//       the other waves form the Q K^T tiles (registers)
+//   P2  A = (I + L)^{-1} in two steps: each wave inverts one 16x16 diagonal block in fp32 on
+//       MFMA, as (I - L)(I + L^2)(I + L^4)(I + L^8) (the block is nilpotent); after a barrier,
+//       wave j forms block column j of A - I by 16x16x16 MFMA merges.  The Q K^T tiles are
+//       spread over the waves (1, 3, 3, 3: wave 0 has the longest merge chain)
 //   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
 //       K^T operands come from the row-major K tile through LDS transpose reads
 //   P4  P (bf16 hi/lo) to LDS, over the dead (A - I) tiles
