@@ -28,7 +28,8 @@
 // x 32 dv columns).  Per chunk:
 //   P0  stage K (loaded one chunk ahead, with g and beta); gate cumsum and the exp2 tables;
 //       issue this chunk's Q and V loads and the next chunk's K, g, beta loads
-//   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L^T (fp32) in LDS;
+//   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L: the diagonal
+//       blocks transposed in fp32, the off-diagonal blocks row-major in bf16 (LDS);
 //       stage Q
 //   P2  A = (I + L)^{-1} in two steps: each wave inverts one 16x16 diagonal block in fp32 on
 //       MFMA, as (I - L)(I + L^2)(I + L^4)(I + L^8) (the block is nilpotent); after a barrier,
