@@ -11,7 +11,7 @@
 // wave w keeps S^T for its 32 columns in MFMA accumulators and per chunk computes
 //     U' = U0 + (-W) S^T,   Y = Q S^T
 //     S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K
-//     O  = diag(q_scale e^gamma) Y + P U'      (stored transposed: one token per lane)
+//     O  = diag(q_scale e^gamma) Y + P U'      (stored as 32-bit words of two value columns)
 // with the same operand splits as the fused kernel (U' hi / lo in the state update, P and U'
 // hi / lo in P U').
 //
