@@ -286,7 +286,7 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         const int r = (int)(blockIdx.x / 8);
         const int u = (r / G) * 8 + (int)(blockIdx.x % 8);
         if (u >= B * Hqk) return;
-        b = ordered ? seq_at(u / Hqk) : u / Hqk;
+        b = (ordered & 1) ? seq_at(u / Hqk) : u / Hqk;
         hv = (u % Hqk) * G + r % G;
     }
     (void)order;
@@ -389,13 +389,14 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         stage();
     }
 
-    // With unequal lengths (ordered), the two workgroups that share a CU take turns at issue
-    // priority chunk by chunk, by the parity of their wave slot: otherwise the one dispatched
-    // first keeps it throughout.  Measured on 64 hits of 205 to 6,554 tokens: 1.43 -> 1.39 ms;
-    // with equal lengths it measured 1-2% slower, so it is off there.
+    // With unequal lengths, or when all workgroups fit in one round, the two workgroups that
+    // share a CU take turns at issue priority chunk by chunk, by the parity of their wave slot:
+    // otherwise the one dispatched first keeps it throughout.  Measured on 64 hits of 205 to
+    // 6,554 tokens: 1.43 -> 1.39 ms.  With equal lengths over several rounds it measured 1-2%
+    // slower (an early finisher lets the next round start sooner), so it is off there.
     const int slot = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 4) & 1);   // HW_ID wave_id, bit 0
     for (int c = c_begin; c < c_end; ++c) {
-        if (!PREP && ordered) {
+        if (!PREP && (ordered & 2)) {
             if ((slot + c) & 1) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
         }
@@ -893,7 +894,14 @@ hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, const SeqOrde
     const dim3 block(DV * 2);
     SeqOrder ord{};
     if (order) ord = *order;
-    hipLaunchKernelGGL(kern, grid, block, smem, stream, ord, order ? 1 : 0,
+    // flags: bit 0, sequences in the given order; bit 1, the two workgroups of a CU take
+    // turns at issue priority (unequal lengths, or one partial round of workgroups)
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const bool one_round = cus > 0 && blocks <= 2LL * cus;
+    const int flags = (order ? 1 : 0) | ((order || one_round) ? 2 : 0);
+    hipLaunchKernelGGL(kern, grid, block, smem, stream, ord, flags,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.g, a.beta, a.cu_seqlens,
                        a.B, a.Hqk, a.Hv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
                        a.state_in, a.state_identity, a.state_out, (bf16*)a.o,
