@@ -55,6 +55,8 @@ def parse():
                    choices=["group", "batched_r05", "batched", "single_hit", "varlen",
                             "fidelity", "full_prefix", "decode", "overlap"])
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--schedule", default="auto", choices=["auto", "fused", "split"],
+                   help="schedule of the bf16 recurrence (tr_gdn_set_schedule)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU-baseline sample time")
     p.add_argument("--flush-cache", action="store_true",
@@ -115,8 +117,8 @@ def copy_calibration():
 # ---------------------------------------------------------------- counting rules
 def gdn_bytes(T, B, Hqk, Hv, dk, dv, with_o=True, with_state_in=False, elt=2):
     """Algorithmic HBM bytes of one tr_gdn_replay launch: every input read once, every
-    output written once (q and k once per query/key head)."""
-    per_tok = Hqk * 2 * dk * elt + Hv * dv * elt + Hv * 8 + (Hv * dv * elt if with_o else 0)
+    output written once (q and k once per query/key head; a state-only launch reads no q)."""
+    per_tok = Hqk * (2 if with_o else 1) * dk * elt + Hv * dv * elt + Hv * 8 + (Hv * dv * elt if with_o else 0)
     state = B * Hv * dv * dk * 4 * (2 if with_state_in else 1)
     return T * per_tok + state
 
@@ -235,6 +237,36 @@ def time_steps(step, steps, warmup, flush):
     return float(np.mean(per)), None, per
 
 
+def step_stats(step, steps, warmup):
+    """Per-step mean, median and min (ms) with HIP events around each step: warm (inputs
+    resident in HBM, steps back to back) and with the 256 MB MALL flushed before each step by a
+    512 MiB fill of a scratch buffer (the fill is outside the events)."""
+    import torch
+    out = {}
+    mean, med, mn = time_launches(step, steps, warmup)
+    out["warm"] = dict(mean_ms=mean, median_ms=med, min_ms=mn, reps=steps)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    per = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    del scratch
+    out["flushed"] = dict(mean_ms=float(np.mean(per)), median_ms=float(np.median(per)), min_ms=float(np.min(per)),
+                          reps=steps)
+    return out
+
+
+def fused_kernel_name(dk, dv, schedule):
+    """The kernel a fused-schedule tr_gdn_replay launch runs."""
+    return "gdn_chunk_bf16_kernel<%d,%d>" % (dk, dv)
+
+
 def time_launches(fn, steps, warmup):
     """Average duration of one launch of fn() with HIP events on the current stream."""
     import torch
@@ -298,6 +330,60 @@ def _busy_gpu(torch, seconds):
 
 
 # ---------------------------------------------------------------- CPU baseline
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+_ONE_CORE = r"""
+import json, sys, time
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import oracle
+z = np.load(sys.argv[2])
+kind, min_s = sys.argv[3], float(sys.argv[4])
+done, elapsed, units = 0, 0.0, 0
+while elapsed < min_s or units == 0:
+    t0 = time.perf_counter()
+    if kind == "gdn":
+        oracle.gdn(z["q"], z["k"], z["v"], z["g"], z["beta"], z["cu"])
+    else:
+        L = int(z["L"])
+        ws = [[{k: z["%s_%d" % (k, l)] for k in ("w_qk", "w_v", "w_a", "w_b", "w_o")} for l in range(L)]]
+        oracle.group(z["h"], ws, int(z["Hqk"]), int(z["Hv"]), int(z["dk"]), int(z["dv"]))
+    elapsed += time.perf_counter() - t0
+    done += int(z["token_heads"])
+    units += 1
+print(json.dumps(dict(value=done / elapsed, seconds=elapsed, units=units, threads=oracle.num_threads())))
+"""
+
+
+def cpu_one_core(arrays, kind, min_seconds, unit_desc):
+    """The same oracle on one core (OpenMP and BLAS limited to one thread, in a child process
+    that loads one unit of the workload from a temporary file), repeated until min_seconds."""
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "unit.npz")
+        np.savez(path, **arrays)
+        env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+        res = subprocess.run([sys.executable, "-c", _ONE_CORE, HERE, path, kind, str(min_seconds)],
+                             capture_output=True, text=True, env=env, timeout=600)
+    if res.returncode != 0:
+        return dict(error=res.stderr[-500:])
+    out = json.loads(res.stdout.strip().splitlines()[-1])
+    out["sample"] = "%d repetition(s) of %s" % (out.pop("units"), unit_desc)
+    out["seconds"] = round(out["seconds"], 2)
+    out["cores"] = out.pop("threads")
+    return out
+
+
 def cpu_baseline(w, min_seconds):
     """The fp64 oracle on whole (sequence, all heads) units of the same workload until at
     least min_seconds of CPU time has accumulated."""
@@ -323,8 +409,14 @@ def cpu_baseline(w, min_seconds):
                 break
         sample = "%d of %d sequences x %d heads (%d token-heads), fp64 token loop" % (
             units, len(order), spec["Hv"], done_th)
+        n0 = int(w["lens"][0])
+        unit = {k: np64(t[:n0]) for k, t in (("q", inp.q), ("k", inp.k), ("v", inp.v), ("g", inp.g),
+                                              ("beta", inp.beta))}
+        unit.update(cu=np.array([0, n0], dtype=np.int32), token_heads=n0 * spec["Hv"])
+        one = cpu_one_core(unit, "gdn", min_seconds / 4,
+                           "sequence 0 (%d tokens x %d heads), fp64 token loop" % (n0, spec["Hv"]))
         return dict(value=done_th / elapsed, unit="token-heads/s", cores=oracle.num_threads(), kind="oracle",
-                    sample=sample, seconds=round(elapsed, 2))
+                    sample=sample, seconds=round(elapsed, 2), cpu_model=cpu_model(), one_core=one)
     # group: whole groups (all layers) through the chain oracle
     spec, gi = w["spec"], w["inputs"]
     done_th, elapsed, units = 0, 0.0, 0
@@ -341,8 +433,15 @@ def cpu_baseline(w, min_seconds):
             break
     sample = "%d of %d groups x %d layers x %d heads x %d tokens, fp64" % (
         units, spec["G"], spec["L"], spec["Hv"], n_cpu)
+    unit = dict(h=np64(gi.h_tail[0:1, :n_cpu]), L=spec["L"], Hqk=spec["Hqk"], Hv=spec["Hv"], dk=spec["dk"],
+                dv=spec["dv"], token_heads=n_cpu * spec["Hv"] * spec["L"])
+    for li in range(spec["L"]):
+        for k, t in gi.weights[0][li].items():
+            unit["%s_%d" % (k, li)] = np64(t)
+    one = cpu_one_core(unit, "group", min_seconds / 4,
+                       "group 0 (%d layers x %d heads x %d tokens), fp64" % (spec["L"], spec["Hv"], n_cpu))
     return dict(value=done_th / elapsed, unit="token-heads/s", cores=oracle.num_threads(), kind="oracle",
-                sample=sample, seconds=round(elapsed, 2))
+                sample=sample, seconds=round(elapsed, 2), cpu_model=cpu_model(), one_core=one)
 
 
 # ---------------------------------------------------------------- next-row modes
@@ -546,6 +645,7 @@ def main():
         return
     import linear_attention_state_amd as tr
     tr.lib()   # fails loudly if the HIP library is not built
+    tr.set_gdn_schedule(args.schedule)
     special = {"fidelity": run_fidelity, "decode": run_decode, "full_prefix": run_full_prefix,
                "overlap": run_overlap}
     if args.workload in special:
@@ -572,7 +672,7 @@ def main():
                        workspace=w["workspace"])
         k_mean, k_med, k_min = time_launches(kern, max(args.steps, 10), 2)
         if w["workspace"] is None:
-            kname = "gdn_chunk_bf16_kernel<%d,%d>" % (spec["dk"], spec["dv"])
+            kname = fused_kernel_name(spec["dk"], spec["dv"], args.schedule)
         else:
             # split schedule: one tr_gdn_replay call is the prep kernel then the state scan
             kname = "gdn split schedule <%d,%d> (gdn_chunk_bf16_kernel prep + gdn_scan_split_kernel)" % (
@@ -592,7 +692,9 @@ def main():
         G, L, n = spec["G"], spec["L"], w["n"]
         token_heads = G * L * n * spec["Hv"]
         gemm = group_gemm_flops(G, L, n, spec["d_model"], spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
-        gdn_f = L * G * gdn_useful_flops([n], spec["Hv"], spec["dk"], spec["dv"])
+        # the last layer of a group is state-only: no Q K^T, Q S^T or P U'
+        gdn_f = G * ((L - 1) * gdn_useful_flops([n], spec["Hv"], spec["dk"], spec["dv"])
+                     + gdn_useful_flops([n], spec["Hv"], spec["dk"], spec["dv"], with_o=False))
         flops = gemm + gdn_f
         roof = group_roofline(w, args)
         config = dict(workload=args.workload, groups=G, layers_per_group=L, tokens_per_group=n,
@@ -621,11 +723,48 @@ def main():
     }
     if host_ms is not None:
         line["host_ms_per_step"] = host_ms
+    line["timing"] = step_stats(step, args.steps, 2)
+    line["timing"]["note"] = ("per-step HIP events: warm = inputs resident, steps back to back; flushed = "
+                              "a 512 MiB scratch fill before each step evicts the 256 MB MALL")
+    if args.workload == "group":
+        line["target_shape"] = target_shape(args)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_seconds)
         cb["gpu_speedup"] = line["value"] / cb["value"]
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
+
+
+def target_shape(args):
+    """The recurrence alone at the batched 5% shape (36 instances x 32 value heads sharing 16
+    query/key heads, 1,639 tail tokens of a 32,768-token prefix): one tr_gdn_replay launch,
+    timed warm and with the MALL flushed, against the HBM roofline of its compulsory bytes."""
+    import torch
+    from linear_attention_state_amd import gdn_replay
+    w = build_workload("batched_r05", args.seed)
+    spec, inp = w["spec"], w["inputs"]
+    B, T = len(w["lens"]), int(sum(w["lens"]))
+    S = torch.empty((B, spec["Hv"], spec["dv"], spec["dk"]), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, spec["Hv"], spec["dv"]), dtype=torch.bfloat16, device="cuda")
+    cu_host = torch.from_numpy(np.concatenate([[0], np.cumsum(w["lens"])]).astype(np.int32))
+
+    def launch():
+        gdn_replay(inp.q, inp.k, inp.v, inp.g, inp.beta, cu_host, cu_seqlens_dev=w["cu_dev"], state_out=S, o=o)
+    st = step_stats(launch, max(args.steps, 10), 2)
+    nbytes = gdn_bytes(T, B, spec["Hqk"], spec["Hv"], spec["dk"], spec["dv"])
+    kname = fused_kernel_name(spec["dk"], spec["dv"], args.schedule)
+    t = st["warm"]["mean_ms"] * 1e-3
+    out = dict(workload="batched_r05", hits=B, tokens_per_hit=w["lens"][0], Hqk=spec["Hqk"], Hv=spec["Hv"],
+               dk=spec["dk"], dv=spec["dv"], token_heads=T * spec["Hv"], kernel=kname,
+               value=T * spec["Hv"] / t, unit="token-heads/s", avg_launch_us=st["warm"]["mean_ms"] * 1e3,
+               timing=st, roofline=dict(bound="hbm", achieved=nbytes / t / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                                        frac=nbytes / t / 1e9 / HBM_PEAK_GBS, algorithmic_bytes=nbytes,
+                                        traffic=measured_traffic(kname, "batched_r05")))
+    tf = st["flushed"]["mean_ms"] * 1e-3
+    out["roofline"]["frac_flushed"] = nbytes / tf / 1e9 / HBM_PEAK_GBS
+    del w, inp, S, o
+    torch.cuda.empty_cache()
+    return out
 
 
 def group_roofline(w, args):
@@ -667,9 +806,9 @@ def group_roofline(w, args):
     kernels = {
         "gemm_tn_kernel<layer_in> (RMSNorm'd hidden x [W_qk|W_v|W_a|W_b]^T, fused L2 norm / gates)":
             dict(avg_us=t_proj[0] * 1e3, per_step=L, bound="mfma", work=proj_flops),
-        "gdn_chunk_bf16_kernel<128,128> (with outputs)":
+        fused_kernel_name(dk, dv, args.schedule) + " (with outputs)":
             dict(avg_us=t_gdn_o[0] * 1e3, per_step=L - 1, bound="hbm", work=gdn_o_bytes),
-        "gdn_chunk_bf16_kernel<128,128> (state only)":
+        fused_kernel_name(dk, dv, args.schedule) + " (state only)":
             dict(avg_us=t_gdn_s[0] * 1e3, per_step=1, bound="hbm", work=gdn_s_bytes),
         "gemm_tn_kernel<residual> (o W_o^T + x)":
             dict(avg_us=t_out[0] * 1e3, per_step=L - 1, bound="mfma", work=out_flops),

@@ -50,67 +50,17 @@
 // state split along dv.
 // An accumulator feeds the next product directly as its B operand: the contraction index
 // is permuted the same way on both operands (see kperm()).
-#include "internal.h"
+#include "gdn_mfma.h"
 
 #include <type_traits>
 
 namespace tr {
 namespace {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace gdn;
 
-constexpr int CH = 64;                 // tokens per chunk
 constexpr int RS_T = CH + 8;           // row stride (elements) of 64-column bf16 tiles
 constexpr int RS_L = CH + 4;           // row stride of the fp32 L tile
-
-__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16k32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-// fp32 16x16 product on 16x16x4 fp32 MFMA.  X in row layout (lane (m, g = l / 16) holds
-// X[m][4g .. 4g+3]) times Y in accumulator layout (lane (n, g) holds Y[4g .. 4g+3][n]),
-// plus C, gives the accumulator layout; step s pairs contraction index 4g + s on both sides.
-// With the operands swapped (Y's registers as X, X's as Y) the same call gives the product
-// transposed, i.e. in row layout.
-__device__ __forceinline__ f32x4 mm16f(const f32x4& xrow, const f32x4& yacc, f32x4 c) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[s], yacc[s], c, 0, 0, 0);
-    return c;
-}
-__device__ __forceinline__ f32x16 zero16() {
-    f32x16 z;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = 0.f;
-    return z;
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane group, lane
-// a + 4p supplies the address of row R_p, columns [c + 4a, c + 4a + 4) of a row-major
-// tile; lane 4a + b then receives column c + 4a + b at rows R_0..R_3.
-__device__ __forceinline__ bf16x4 lds_tr4(const bf16* p) {
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(p));
-    return __builtin_bit_cast(bf16x4, r);
-}
-__device__ __forceinline__ bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { r[i] = lo[i]; r[4 + i] = hi[i]; }
-    return r;
-}
 
 // 32x32x16 MFMA layouts (lane l, half h = l / 32):
 //   A operand: row l % 32, k = 8h + i;  B operand: column l % 32, k = 8h + i;
@@ -140,37 +90,6 @@ __device__ __forceinline__ bf16x8 acc_to_b(const f32x16& t, int s) {
     for (int i = 0; i < 8; ++i) r[i] = (bf16)t[8 * (s & 1) + i];
     return r;
 }
-__device__ __forceinline__ bf16x4 to_bf4(const f32x4& x, float sign) {
-    bf16x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (bf16)(sign * x[i]);
-    return r;
-}
-
-// Workgroup barrier for LDS hand-offs only.  __syncthreads() would also wait for every
-// outstanding global load, including the next chunk's prefetch issued just before it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-    float y;
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, false));
-    x += y;   // row_shr:1
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
-    x += y;   // row_shr:2
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
-    x += y;   // row_shr:4
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
-    x += y;   // row_shr:8
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
-    x += y;   // row_bcast:15 into rows 1 and 3
-    y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
-    x += y;   // row_bcast:31 into rows 2 and 3
-    return x;
-}
-
 template <int DK, int DV>
 struct Smem {
     bf16 K[CH][DK + 16];        // key rows (padding keeps the transpose reads conflict-free)
@@ -197,23 +116,8 @@ struct Smem {
     float dec[CH];              // e^{gamma_last - gamma_t}
 };
 
-// Four consecutive table entries starting at a multiple of 4.
-__device__ __forceinline__ f32x4 tab4(const float* t, int i) { return *reinterpret_cast<const f32x4*>(t + i); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // WITH_O: per-token outputs are produced (Q is loaded, Q K^T and P formed, O stored); without
 // them the kernel is the state-only scan.
-// Sequence at longest-first rank `rank`: the order travels as the kernel's first argument and
-// is read through the kernel-argument segment (indexing the by-value argument with a variable
-// would copy it to scratch memory).
-__device__ __forceinline__ int seq_at(int rank) {
-    typedef const __attribute__((address_space(4))) uint16_t kshort;
-    return ((kshort*)__builtin_amdgcn_kernarg_segment_ptr())[rank];
-}
-
 template <int DK, int DV, bool WITH_O, bool PREP>
 __global__ void __launch_bounds__(DV * 2, 2)
 gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -238,7 +142,6 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
     // product chains.  Tiles are numbered row by row: (0,0) (1,0) (1,1) (2,0) ...
     constexpr int QK_PER_WAVE = NW == 4 ? 3 : 6;
     auto qk_begin = [](int w) { return NW == 4 ? (w == 0 ? 0 : 3 * w - 2) : (w == 0 ? 0 : (w == 1 ? 4 : 10)); };
-    constexpr float LOG2E = 1.4426950408889634f;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem<DK, DV>& sm = *reinterpret_cast<Smem<DK, DV>*>(smem_raw);
@@ -882,9 +785,9 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
 
 template <int DK, int DV, bool WITH_O, bool PREP>
 hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, const SeqOrder* order, hipStream_t stream) {
-    auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O, PREP>;
+    constexpr auto kern = gdn_chunk_bf16_kernel<DK, DV, WITH_O, PREP>;
     const size_t smem = sizeof(Smem<DK, DV>);
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const hipError_t e = ensure_dynamic_smem<kern>(smem);
     if (e != hipSuccess) return e;
     // a multiple of 8 blocks (one share per XCD); fused: ceil(units / 8) rounds of 8 units
     const long long units = (long long)a.B * a.Hqk;
@@ -896,9 +799,7 @@ hipError_t launch_variant(const GdnArgs& a, const SplitPlan* plan, const SeqOrde
     if (order) ord = *order;
     // flags: bit 0, sequences in the given order; bit 1, the two workgroups of a CU take
     // turns at issue priority (unequal lengths, or one partial round of workgroups)
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const int cus = device_cu_count();
     const bool one_round = cus > 0 && blocks <= 2LL * cus;
     const int flags = (order ? 1 : 0) | ((order || one_round) ? 2 : 0);
     hipLaunchKernelGGL(kern, grid, block, smem, stream, ord, flags,

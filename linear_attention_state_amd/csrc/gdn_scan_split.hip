@@ -347,9 +347,9 @@ constexpr int kScanWaves = 2;   // waves (32 value columns each) per scan workgr
 
 template <int DK, int DV, bool WITH_O>
 hipError_t launch_scan(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream) {
-    auto kern = gdn_scan_split_kernel<DK, DV, kScanWaves, WITH_O>;
+    constexpr auto kern = gdn_scan_split_kernel<DK, DV, kScanWaves, WITH_O>;
     const size_t smem = 2 * sizeof(Stage<DK, kScanWaves>);
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const hipError_t e = ensure_dynamic_smem<kern>(smem);
     if (e != hipSuccess) return e;
     const long long items = (long long)a.B * a.Hv * (DV / (32 * kScanWaves));
     const dim3 grid((unsigned)((items + 7) / 8 * 8));

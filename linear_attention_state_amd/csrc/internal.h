@@ -5,7 +5,35 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace tr {
+
+// hipFuncSetAttribute(max dynamic shared memory) once per (kernel, device) in the process
+// rather than on every launch.
+template <auto KERN>
+hipError_t ensure_dynamic_smem(size_t smem) {
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (done.load(std::memory_order_acquire) & (1ull << dev)) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess) done.fetch_or(1ull << dev, std::memory_order_acq_rel);
+    return e;
+}
+
+// Compute units of the current device, queried once per device (0 if the query fails).
+inline int device_cu_count() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // One tr_gdn_replay request after host-side validation.
 struct GdnArgs {

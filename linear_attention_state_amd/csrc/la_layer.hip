@@ -415,8 +415,7 @@ unsigned grid_for(int tiles) { return (unsigned)(((tiles + 7) / 8) * 8); }
 
 template <int EPI>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
-    const hipError_t e = hipFuncSetAttribute((const void*)gemm_tn_kernel<EPI>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    const hipError_t e = ensure_dynamic_smem<gemm_tn_kernel<EPI>>(SMEM_BYTES);
     if (e != hipSuccess) return e;
     const int tiles = p.G * p.n_mt * p.n_nt;
     hipLaunchKernelGGL(gemm_tn_kernel<EPI>, dim3(grid_for(tiles)), dim3(NTHREADS), SMEM_BYTES, stream, p);

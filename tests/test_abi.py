@@ -177,3 +177,125 @@ def test_decode_rejects_bad_arguments():
         args[idx] = val
         st = lib.tr_gdn_decode(*args)
         assert st == status and "tr_gdn_decode" in lib.tr_last_error().decode(), (idx, val)
+
+
+def _weights(n, null_field=None, at=None):
+    """A host array of n tr_la_weights with fake (never dereferenced) device pointers."""
+    arr = (C.LaWeights * n)()
+    for i in range(n):
+        for f in ("w_qk", "w_v", "w_a", "w_b", "w_o"):
+            setattr(arr[i], f, 0x1000 + 0x100 * i)
+        if null_field and (at is None or at == i):
+            setattr(arr[i], null_field, None)
+    return arr
+
+
+def call_group(**over):
+    args = dict(h=FAKE, G=2, L=3, n=100, d=256, Hqk=2, Hv=4, dk=128, dv=128, eps=1e-6, states=FAKE)
+    args.update(over)
+    w = over.get("w", _weights(max(args["G"], 1) * max(args["L"], 1)))
+    lib = L.lib()
+    need = lib.tr_group_replay_workspace_size(args["G"], args["L"], args["n"], args["d"], args["Hqk"], args["Hv"],
+                                              args["dk"], args["dv"])
+    ws_bytes = args.get("ws_bytes", need)
+    st = lib.tr_group_replay(args["h"], ctypes.cast(w, ctypes.c_void_p) if w is not None else None,
+                             args["G"], args["L"], args["n"], args["d"], args["Hqk"], args["Hv"], args["dk"],
+                             args["dv"], args["eps"], args["states"], args.get("ws", FAKE), ws_bytes, None)
+    return st, lib.tr_last_error().decode(), need
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), 1), (dict(L=0), 1), (dict(n=0), 1),
+    (dict(Hv=3), 1),                                   # not a multiple of Hqk
+    (dict(Hqk=1, Hv=65), 2),                           # more value heads than the layer path takes
+    (dict(dk=64), 2), (dict(dv=64), 2),
+    (dict(d=200), 2), (dict(d=64), 2),                 # d_model not a multiple of 128
+    (dict(eps=-1.0), 1), (dict(eps=float("inf")), 1),
+    (dict(h=None), 1), (dict(states=None), 1), (dict(w=None), 1),
+    (dict(w=_weights(6, "w_qk", at=4)), 1),            # a null projection weight in group 1, layer 1
+    (dict(w=_weights(6, "w_o", at=1)), 1),             # a null W_o where its output feeds a layer
+])
+def test_group_replay_rejects_bad_arguments(over, status):
+    st, msg, _ = call_group(**over)
+    assert st == status and "tr_group_replay" in msg
+
+
+def test_group_replay_workspace_and_last_layer_w_o():
+    st, msg, need = call_group(ws_bytes=0)
+    assert st == C.TR_ERR_WORKSPACE and need > 0
+    st, msg, need = call_group(ws_bytes=need - 1)
+    assert st == C.TR_ERR_WORKSPACE
+    st, msg, _ = call_group(ws=None)
+    assert st == C.TR_ERR_WORKSPACE
+    # the last layer's W_o is never read (its outputs are not produced): a null one is fine, so
+    # this request fails only at the (deliberately short) workspace
+    st, msg, need = call_group(w=_weights(6, "w_o", at=2), ws_bytes=need - 1)
+    assert st == C.TR_ERR_WORKSPACE
+
+
+def _wptrs(structs):
+    """tr_la_weights* const* over a structure array."""
+    ptrs = (ctypes.c_void_p * len(structs))(*[ctypes.addressof(s) for s in structs])
+    return ctypes.cast(ptrs, ctypes.c_void_p), ptrs
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), 1), (dict(n=0), 1), (dict(Hv=3), 1), (dict(Hqk=1, Hv=65), 2), (dict(dk=64), 2),
+    (dict(d=300), 2), (dict(eps=float("nan")), 1), (dict(x=None), 1), (dict(q=None), 1), (dict(beta=None), 1),
+    (dict(null="w_v"), 1), (dict(ws_bytes=-1), 3),
+])
+def test_layer_inputs_rejects_bad_arguments(over, status):
+    lib = L.lib()
+    a = dict(x=FAKE, G=2, n=100, d=256, Hqk=2, Hv=4, dk=128, dv=128, eps=1e-6, q=FAKE, k=FAKE, v=FAKE,
+             g=FAKE, beta=FAKE)
+    a.update(over)
+    structs = _weights(max(a["G"], 1), a.get("null"), at=1 if a.get("null") else None)
+    wp, keep = _wptrs(structs)
+    need = lib.tr_la_layer_inputs_workspace_size(a["G"], a["n"], a["d"])
+    ws_bytes = need - 1 if a.get("ws_bytes") == -1 else need
+    st = lib.tr_la_layer_inputs(a["x"], wp, a["G"], a["n"], a["d"], a["Hqk"], a["Hv"], a["dk"], a["dv"], a["eps"],
+                                a["q"], a["k"], a["v"], a["g"], a["beta"], FAKE, ws_bytes, None)
+    assert st == status and "tr_la_layer_inputs" in lib.tr_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), 1), (dict(Hv=3), 1), (dict(Hqk=1, Hv=65), 2), (dict(dv=64), 2), (dict(d=100), 2),
+    (dict(y=None), 1), (dict(v=None), 1), (dict(null="w_b"), 1),
+])
+def test_project_rejects_bad_arguments(over, status):
+    lib = L.lib()
+    a = dict(y=FAKE, G=2, n=100, d=256, Hqk=2, Hv=4, dk=128, dv=128, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE)
+    a.update(over)
+    structs = _weights(max(a["G"], 1), a.get("null"), at=0 if a.get("null") else None)
+    wp, keep = _wptrs(structs)
+    st = lib.tr_la_project(a["y"], wp, a["G"], a["n"], a["d"], a["Hqk"], a["Hv"], a["dk"], a["dv"],
+                           a["q"], a["k"], a["v"], a["g"], a["beta"], None)
+    assert st == status and "tr_la_project" in lib.tr_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), 1), (dict(n=0), 1), (dict(d=129), 2), (dict(Hv=1, dv=32), 2), (dict(x_in=None), 1),
+    (dict(o=None), 1), (dict(x_out=None), 1), (dict(null="w_o"), 1),
+])
+def test_output_residual_rejects_bad_arguments(over, status):
+    lib = L.lib()
+    a = dict(x_in=FAKE, o=FAKE, G=2, n=100, d=256, Hv=4, dv=128, x_out=FAKE)
+    a.update(over)
+    structs = _weights(max(a["G"], 1), a.get("null"), at=1 if a.get("null") else None)
+    wp, keep = _wptrs(structs)
+    st = lib.tr_la_output_residual(a["x_in"], a["o"], wp, a["G"], a["n"], a["d"], a["Hv"], a["dv"], a["x_out"], None)
+    assert st == status and "tr_la_output_residual" in lib.tr_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(G=0), 1), (dict(n=0), 1), (dict(d=96), 2), (dict(eps=-0.5), 1), (dict(x=None), 1), (dict(y=None), 1),
+    (dict(gain=None), 1),
+])
+def test_rmsnorm_rejects_bad_arguments(over, status):
+    lib = L.lib()
+    a = dict(x=FAKE, G=2, n=100, d=256, eps=1e-6, y=FAKE)
+    a.update(over)
+    gains = (ctypes.c_void_p * 2)(None, None)
+    gp = a["gain"] if "gain" in a else ctypes.cast(gains, ctypes.c_void_p)
+    st = lib.tr_rmsnorm(a["x"], gp, a["G"], a["n"], a["d"], a["eps"], a["y"], None)
+    assert st == status and "tr_rmsnorm" in lib.tr_last_error().decode()
