@@ -66,7 +66,12 @@ def l2norm_heads(x, n_heads, d_head):
 
 def layer_inputs(x, w, Hqk, Hv, dk, dv, eps):
     """Projections of one LA layer: returns bf16-valued q, k, v and fp32-valued g, beta."""
-    y = round_bf16(rmsnorm(x, w.get("rms_gain"), eps))
+    return project(round_bf16(rmsnorm(x, w.get("rms_gain"), eps)), w, Hqk, Hv, dk, dv)
+
+
+def project(y, w, Hqk, Hv, dk, dv):
+    """The projections of one LA layer from its normalised hidden y (bf16 values)."""
+    y = np.asarray(y, dtype=np.float64)
     qk = y @ np.asarray(w["w_qk"], dtype=np.float64).T
     q = round_bf16(l2norm_heads(qk[:, : Hqk * dk], Hqk, dk) * dk ** -0.5)
     k = round_bf16(l2norm_heads(qk[:, Hqk * dk:], Hqk, dk))
