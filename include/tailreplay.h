@@ -131,6 +131,28 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
                         const float* state_in, float* state_out, void* o,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * tr_gdn_replay_noalloc -- tr_gdn_replay for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, layouts, results and errors as tr_gdn_replay, without the workspace: when
+ * the schedule takes the split path, its records go to a device array of
+ * TR_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no host or device allocating routine; its
+ * first call on a device looks the array's address up once).  A request whose records exceed
+ * TR_NOALLOC_SCRATCH_BYTES (tr_gdn_replay_workspace_size tells) returns TR_ERR_WORKSPACE before
+ * anything is enqueued; the fused schedule needs no scratch at any size.  The records are
+ * written in full before they are read, so nothing needs clearing between calls.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race on it. */
+#define TR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tr_status tr_gdn_replay_noalloc(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                                int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                                tr_dtype dt, float q_scale,
+                                const float* state_in, float* state_out, void* o, void* stream);
+
 /* Bytes of workspace tr_gdn_replay needs for this request under the current schedule
  * (0 when it needs none).  Arguments as for tr_gdn_replay; T is cu_seqlens_host[B].
  * Returns 0 and sets tr_last_error() for invalid arguments. */

@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libtailreplay.so")
 
 TR_OK, TR_ERR_INVALID_ARG, TR_ERR_UNSUPPORTED, TR_ERR_WORKSPACE, TR_ERR_HIP = range(5)
 TR_BF16, TR_F32 = 0, 1
+TR_NOALLOC_SCRATCH_BYTES = 64 << 20   # the header's TR_NOALLOC_SCRATCH_BYTES
 TR_SCHEDULE_AUTO, TR_SCHEDULE_FUSED, TR_SCHEDULE_SPLIT = 0, 1, 2
 
 # Every symbol the header declares: (name, restype, argtypes).
@@ -36,6 +37,9 @@ SIGNATURES = {
     "tr_gdn_replay": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
                                      _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tr_gdn_replay_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                             _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
+                                             _vp, _vp, _vp, _vp]),
     "tr_gdn_replay_workspace_size": (_sz, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]),
     "tr_gdn_set_schedule": (ctypes.c_int, [ctypes.c_int]),
     "tr_gdn_get_schedule": (ctypes.c_int, []),

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -268,14 +269,46 @@ size_t tr_gdn_replay_workspace_size(const int32_t* cu_seqlens_host, int32_t B, i
     return use_split(B, Hv, dv, dt) ? split_workspace_bytes(B, cu_seqlens_host[B], Hv, dk, dv) : 0;
 }
 
-tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
-                        const float* g, const float* beta,
-                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
-                        int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
-                        tr_dtype dt, float q_scale,
-                        const float* state_in, float* state_out, void* o,
-                        void* workspace, size_t workspace_bytes, void* stream) {
-    static const char* fn = "tr_gdn_replay";
+}  // extern "C"
+
+namespace {
+
+// Device scratch of tr_gdn_replay_noalloc: the split schedule's records for requests up to
+// kNoallocScratchBytes, in a file-scope device array that every GPU the library runs on holds
+// until the process ends.  The host-side name is not a device address: its address on each
+// device comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoallocScratchBytes = TR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+tr_status noalloc_scratch(const char* fn, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TR_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(TR_ERR_UNSUPPORTED, "%s: device %d beyond the 64 the library tracks", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TR_ERR_HIP, "%s: hipGetSymbolAddress of the static scratch: %s", fn,
+                        e != hipSuccess ? hipGetErrorString(e) : "null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TR_OK;
+}
+
+// tr_gdn_replay and tr_gdn_replay_noalloc: with noalloc set, the split schedule's records go
+// to the static scratch (workspace arguments unused).
+tr_status gdn_replay_impl(const char* fn, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta,
+                          const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                          int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                          tr_dtype dt, float q_scale,
+                          const float* state_in, float* state_out, void* o,
+                          void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
     int32_t max_len = 0;
     const tr_status st = check_gdn(fn, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, dk, dv, dt, &max_len);
     if (st != TR_OK) return st;
@@ -285,6 +318,15 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     if (T > 0 && (!q || !k || !v || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
     const bool split = use_split(B, Hv, dv, dt);
     const size_t need = split ? split_workspace_bytes(B, T, Hv, dk, dv) : 0;
+    if (noalloc && need > kNoallocScratchBytes)
+        return fail(TR_ERR_WORKSPACE, "%s: the split schedule needs %zu bytes of scratch for this request, more "
+                    "than the %zu the library holds; use tr_gdn_replay with a workspace, or TR_SCHEDULE_FUSED "
+                    "(no scratch)", fn, need, kNoallocScratchBytes);
+    if (noalloc && need > 0) {
+        const tr_status ss = noalloc_scratch(fn, &workspace);
+        if (ss != TR_OK) return ss;
+        workspace_bytes = kNoallocScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace ? workspace_bytes : (size_t)0, need);
     if (need > 0 && ((uintptr_t)workspace & 15) != 0)
@@ -307,9 +349,9 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
             for (int32_t b = 1; b < B && uniform; ++b)
                 uniform = cu_seqlens_host[b + 1] - cu_seqlens_host[b] == cu_seqlens_host[1] - cu_seqlens_host[0];
             if (!uniform) {
-                std::vector<int32_t> idx(B);
+                int32_t idx[tr::kMaxOrdered];
                 for (int32_t b = 0; b < B; ++b) idx[b] = b;
-                std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+                std::stable_sort(idx, idx + B, [&](int32_t x, int32_t y) {
                     return cu_seqlens_host[x + 1] - cu_seqlens_host[x] > cu_seqlens_host[y + 1] - cu_seqlens_host[y];
                 });
                 tr::SeqOrder order{};
@@ -327,6 +369,31 @@ tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
     hipError_t e = plan.cmax > 0 ? tr::launch_gdn_prep_bf16(a, plan, s) : hipSuccess;
     if (e == hipSuccess) e = tr::launch_gdn_scan_split_bf16(a, plan, s);
     return finish_launch(e, s, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+tr_status tr_gdn_replay(const void* q, const void* k, const void* v,
+                        const float* g, const float* beta,
+                        const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                        int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                        tr_dtype dt, float q_scale,
+                        const float* state_in, float* state_out, void* o,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_replay_impl("tr_gdn_replay", q, k, v, g, beta, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, dk, dv,
+                           dt, q_scale, state_in, state_out, o, workspace, workspace_bytes, false, stream);
+}
+
+tr_status tr_gdn_replay_noalloc(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
+                                int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv,
+                                tr_dtype dt, float q_scale,
+                                const float* state_in, float* state_out, void* o, void* stream) {
+    return gdn_replay_impl("tr_gdn_replay_noalloc", q, k, v, g, beta, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv,
+                           dk, dv, dt, q_scale, state_in, state_out, o, nullptr, 0, true, stream);
 }
 
 tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,

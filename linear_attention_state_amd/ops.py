@@ -119,6 +119,40 @@ def gdn_replay(q, k, v, g, beta, cu_seqlens, q_scale: float = 1.0, state_in=None
     return state_out, o
 
 
+def gdn_replay_noalloc(q, k, v, g, beta, cu_seqlens, cu_seqlens_dev, state_out, o=None, q_scale: float = 1.0,
+                       state_in=None, stream=None):
+    """tr_gdn_replay_noalloc: tr_gdn_replay with the split schedule's records in the library's
+    static device scratch.  Every buffer is the caller's (cu_seqlens on the host and its device
+    copy, state_out [B, Hv, dv, dk] fp32, o [T, Hv, dv] or None for state-only); nothing is
+    allocated.  Returns (state_out, o)."""
+    _need(q.is_cuda and k.is_cuda and v.is_cuda and g.is_cuda and beta.is_cuda, "inputs must be on the GPU")
+    _need(q.dtype == k.dtype == v.dtype and q.dtype in _DT, "q, k, v must share dtype bf16 or fp32")
+    _need(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be fp32")
+    for t in (q, k, v, g, beta):
+        _need(t.is_contiguous(), "inputs must be contiguous")
+    _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3, "q, k: [T, Hqk, dk]; v: [T, Hv, dv]")
+    T, Hqk, dk = q.shape
+    _, Hv, dv = v.shape
+    _need(v.shape[0] == T and g.shape == (T, Hv) and beta.shape == (T, Hv), "shape mismatch")
+    _need(cu_seqlens.device.type == "cpu" and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous(),
+          "cu_seqlens: int32 on the host")
+    B = cu_seqlens.numel() - 1
+    _need(cu_seqlens_dev.is_cuda and cu_seqlens_dev.dtype == torch.int32 and cu_seqlens_dev.numel() == B + 1,
+          "cu_seqlens_dev: its int32 device copy")
+    _need(state_out.is_cuda and state_out.dtype == torch.float32 and state_out.is_contiguous()
+          and tuple(state_out.shape) == (B, Hv, dv, dk), "state_out must be [B, Hv, dv, dk] fp32")
+    if state_in is not None:
+        _need(state_in.is_cuda and state_in.dtype == torch.float32 and state_in.is_contiguous()
+              and tuple(state_in.shape) == (B, Hv, dv, dk), "state_in must be [B, Hv, dv, dk] fp32")
+    if o is not None:
+        _need(o.is_cuda and o.dtype == q.dtype and o.is_contiguous() and tuple(o.shape) == (T, Hv, dv),
+              "o must be [T, Hv, dv] in the input dtype")
+    check(lib().tr_gdn_replay_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                      _ptr(cu_seqlens_dev), B, T, Hqk, Hv, dk, dv, _DT[q.dtype], float(q_scale),
+                                      _ptr(state_in), _ptr(state_out), _ptr(o), _stream(stream)))
+    return state_out, o
+
+
 def gdn_transition(k, g, beta, cu_seqlens, cu_seqlens_dev=None, phi_out=None, separate_decay: bool = False,
                    stream=None):
     """Transition products of the packed spans (tr_gdn_transition): the recurrence from S = I
