@@ -459,8 +459,8 @@ def run_fidelity(args):
     |S_a Phi| / |S_m| (both from the GPU path), and the times."""
     import torch
     import synthetic
-    from linear_attention_state_amd import (gdn_replay, gdn_replay_workspace_size, gdn_transition, state_compose,
-                                            tail_seqlens)
+    from linear_attention_state_amd import (gdn_replay, gdn_replay_workspace_size, gdn_transition,
+                                            gdn_transition_workspace_size, state_compose, tail_seqlens)
     spec = synthetic.WORKLOADS["fidelity"]
     m, H, d = spec["m"], spec["Hv"], spec["dk"]
     inp = synthetic.gdn_inputs([m], spec["Hqk"], H, d, d, seed=args.seed, backend="torch", device="cuda")
@@ -491,12 +491,21 @@ def run_fidelity(args):
         def replay():
             gdn_replay(*tail, cu_k, cu_seqlens_dev=cu_k_dev, state_out=S_hat, want_o=False, workspace=ws_k)
         t_rep = time_launches(replay, max(args.steps, 5), 1)[0]
+        # the fp32-input build of the same replay (token-serial fp32 recurrence)
+        tail32 = [t.float() for t in tail[:3]] + tail[3:]
+        S_hat32 = torch.empty_like(S_m)
+
+        def replay_fp32():
+            gdn_replay(*tail32, cu_k, cu_seqlens_dev=cu_k_dev, state_out=S_hat32, want_o=False)
+        t_rep32 = time_launches(replay_fp32, 3, 1)[0]
         psi = torch.empty_like(S_m)
+        n_ws = gdn_transition_workspace_size(cu_k, spec["Hqk"], H, d, torch.bfloat16)
+        ws_phi = torch.empty(n_ws, dtype=torch.uint8, device="cuda") if n_ws else None
 
         def transition():
             return gdn_transition(tail[1], tail[3], tail[4], cu_k, cu_seqlens_dev=cu_k_dev, phi_out=psi,
-                                  separate_decay=True)
-        t_phi = time_launches(transition, 3, 1)[0]
+                                  separate_decay=True, workspace=ws_phi)
+        t_phi = time_launches(transition, max(args.steps, 5), 1)[0]
         _, ls = transition()
         S_a, _ = gdn_replay(*head, torch.tensor([0, a], dtype=torch.int32), want_o=False)
         E = state_compose(S_a, psi)                       # S_a psi; Phi = exp(ls) psi
@@ -506,7 +515,7 @@ def run_fidelity(args):
         log10_exact = ((ls[0].double() + torch.log(torch.linalg.matrix_norm(E[0].double())) - torch.log(nm))
                        / np.log(10)).cpu().numpy()
         res["r=%d/%d" % (rn, rd)] = dict(
-            tail_tokens=k, replay_us=t_rep * 1e3, transition_us=t_phi * 1e3,
+            tail_tokens=k, replay_us=t_rep * 1e3, replay_fp32_inputs_us=t_rep32 * 1e3, transition_us=t_phi * 1e3,
             rel_state_error_max=float(measured.max()), rel_state_error_mean=float(measured.mean()),
             log10_exact_truncation_max=float(log10_exact.max()))
     nbytes = gdn_bytes(m, 1, spec["Hqk"], H, d, d, with_o=False)

@@ -93,7 +93,7 @@ tr_status tr_tail_seqlens(const int64_t* m_host, int32_t B, int32_t r_num, int32
  * and an fp32 state; its results match the token recurrence to within rounding.
  *
  * Arguments
- *   q, k        [device] [T, Hqk, dk]  dtype `dt`, row-major (dk contiguous)
+ *   q, k        [device] [T, Hqk, dk]  dtype `dt`, row-major (dk contiguous), 16-byte aligned
  *   v           [device] [T, Hv,  dv]  dtype `dt`
  *   g           [device] [T, Hv] fp32, log alpha (<= 0 for alpha in (0, 1])
  *   beta        [device] [T, Hv] fp32
@@ -188,16 +188,30 @@ tr_schedule tr_gdn_get_schedule(void);
  *   d             dk = dv = d, in {64, 128}
  *   phi_out       [device] [B, Hv, d, d] fp32 (row-major)
  *   log_scale_out [device] [B, Hv] fp32, or NULL (see above)
+ *   workspace     [device] scratch of at least tr_gdn_transition_workspace_size() bytes,
+ *                 16-byte aligned; may be NULL when that size is 0.  Contents on entry do
+ *                 not matter.
+ *   workspace_bytes  its size
  *   stream        hipStream_t to enqueue on
  * Arithmetic is fp32 token by token for both input types (bf16 keys are converted
  * exactly): a long product of operators keeps every rounding it meets, so the chunked bf16
- * path is not used here.  An empty sequence gives phi_out = I (and log scale 0).
- * Errors: as for tr_gdn_replay.
+ * path is not used here.  The product is associative, so with few (sequence, head) pairs
+ * each span is cut into segments that run side by side from I, and each head's segment
+ * products are then multiplied in order (fp32); the cut depends only on the lengths, Hv and
+ * d.  An empty sequence gives phi_out = I (and log scale 0).
+ * Errors: as for tr_gdn_replay (TR_ERR_WORKSPACE for a missing or short workspace).
  * ------------------------------------------------------------------------------- */
 tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
                             const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
                             int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t d,
-                            tr_dtype dt, float* phi_out, float* log_scale_out, void* stream);
+                            tr_dtype dt, float* phi_out, float* log_scale_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace tr_gdn_transition needs for this request (0 when it needs none).
+ * Arguments as for tr_gdn_transition; T is cu_seqlens_host[B].  Returns 0 and sets
+ * tr_last_error() for invalid arguments. */
+size_t tr_gdn_transition_workspace_size(const int32_t* cu_seqlens_host, int32_t B, int32_t Hqk, int32_t Hv,
+                                        int32_t d, tr_dtype dt);
 
 /* ---------------------------------------------------------------------------------
  * tr_state_compose -- out[n] = exp(log_scale[n]) S_c[n] phi[n] + S_hat[n] for n < N.

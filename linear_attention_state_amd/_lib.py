@@ -44,7 +44,8 @@ SIGNATURES = {
     "tr_gdn_set_schedule": (ctypes.c_int, [ctypes.c_int]),
     "tr_gdn_get_schedule": (ctypes.c_int, []),
     "tr_gdn_transition": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
-                                         _vp, _vp, _vp]),
+                                         _vp, _vp, _vp, _sz, _vp]),
+    "tr_gdn_transition_workspace_size": (_sz, [_vp, _i32, _i32, _i32, _i32, ctypes.c_int]),
     "tr_state_compose": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
     "tr_gdn_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _f32,
                                      _vp, _vp, _vp]),

@@ -144,6 +144,67 @@ hipError_t output_residual(const void* x_in, const void* o, const tr_la_weights*
     return hipSuccess;
 }
 
+// tr_group_replay's workspace, carved as GroupLayout says.
+struct GroupBuffers {
+    bf16 *x, *y, *q, *k, *v, *o;
+    float *g, *beta;
+    GroupBuffers(void* workspace, const GroupLayout& lay) {
+        unsigned char* ws = (unsigned char*)workspace;
+        x = (bf16*)(ws + lay.x); y = (bf16*)(ws + lay.y); q = (bf16*)(ws + lay.q); k = (bf16*)(ws + lay.k);
+        v = (bf16*)(ws + lay.v); o = (bf16*)(ws + lay.o); g = (float*)(ws + lay.g); beta = (float*)(ws + lay.beta);
+    }
+};
+
+// The LA layers of groups [g0, g1) on one stream: every layer from the zero state, the last one
+// state-only.  Each group's rows of the workspace buffers are its own, so disjoint group ranges
+// could run on different streams at once (measured: two halves side by side on two streams were
+// slower than one stream, the projection products already fill the chip).
+hipError_t group_chain(const void* h_tail, const tr_la_weights* const* wp, int32_t g0, int32_t g1, int32_t L,
+                       int32_t n, int32_t d, int32_t Hqk, int32_t Hv, int32_t dk, int32_t dv, float eps,
+                       float* states_out, const GroupBuffers& buf, hipStream_t s) {
+    const int32_t G = g1 - g0;
+    const size_t r0 = (size_t)g0 * n;
+    bf16* x = buf.x + r0 * d;
+    bf16* y = buf.y + r0 * d;
+    bf16* q = buf.q + r0 * Hqk * dk;
+    bf16* k = buf.k + r0 * Hqk * dk;
+    bf16* v = buf.v + r0 * Hv * dv;
+    bf16* o = buf.o + r0 * Hv * dv;
+    float* g = buf.g + r0 * Hv;
+    float* beta = buf.beta + r0 * Hv;
+    const tr_la_weights* const* w = wp + (size_t)g0 * L;
+    const int64_t state_elems = (int64_t)Hv * dv * dk;
+    const void* x_cur = (const bf16*)h_tail + r0 * d;
+    for (int32_t li = 0; li < L; ++li) {
+        const bool last = li == L - 1;
+        // projections in front of the recurrence (stride L through the weight table)
+        hipError_t e = layer_inputs(x_cur, w, L, li, G, n, d, Hqk, Hv, eps, y, q, k, v, g, beta, s);
+        if (e != hipSuccess) return e;
+        // the recurrence from the zero state; the last layer keeps its state only
+        tr::GdnArgs a;
+        a.state_identity = 0;
+        a.log_scale_out = nullptr;
+        a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+        a.cu_seqlens = nullptr; a.uniform_len = n;
+        a.B = G; a.T = G * n; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = 1.0f;
+        a.state_in = nullptr; a.state_out = states_out + ((int64_t)g0 * L + li) * state_elems;
+        a.state_bstride = (int64_t)L * state_elems;
+        a.o = last ? nullptr : o; a.max_len = n;
+        e = tr::launch_gdn_chunk_bf16(a, s);
+        if (e != hipSuccess) return e;
+        if (!last) {
+            e = output_residual(x_cur, o, w, L, li, G, n, d, Hv * dv, x, s);
+            if (e != hipSuccess) return e;
+            x_cur = x;
+        }
+        if (debug_sync()) {
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,6 +305,34 @@ hipError_t launch_gdn(const tr::GdnArgs& a, tr_dtype dt, hipStream_t s) {
     return (dt == TR_BF16) ? tr::launch_gdn_chunk_bf16(a, s) : tr::launch_gdn_token_f32(a, s);
 }
 
+// Segments of tr_gdn_transition.  The product of a span's operators is associative, so with
+// few (sequence, head) pairs to run, each span is cut into segments of seg_len tokens that run
+// side by side from I, and their products are multiplied in order afterwards.  The plan aims
+// the segments at kTransitionWgs workgroups of 16 rows (three per CU on 256 CUs) and depends
+// only on the lengths, the head count and d, so a result does not change with the device.
+constexpr int64_t kTransitionWgs = 768;
+constexpr int64_t kTransitionMinSeg = 128;   // shorter segments cost more to multiply than to run
+constexpr int64_t kTransitionMaxSegs = 16;   // the products are multiplied one after another
+struct TransitionPlan {
+    tr::Segments sg;
+    size_t bytes = 0;
+};
+TransitionPlan transition_plan(const int32_t* cu, int32_t B, int32_t Hv, int32_t d, int32_t max_len) {
+    TransitionPlan p;
+    const int64_t per_seq = (int64_t)Hv * (d / 16);    // workgroups of one sequence's whole span
+    if ((int64_t)B * per_seq * 2 > kTransitionWgs) return p;
+    const int64_t segs = (kTransitionWgs + per_seq - 1) / per_seq;   // segments in all
+    int64_t seg = std::max<int64_t>(((int64_t)cu[B] + segs - 1) / segs, kTransitionMinSeg);
+    seg = std::max<int64_t>(seg, (max_len + kTransitionMaxSegs - 1) / kTransitionMaxSegs);
+    const int64_t smax = (max_len + seg - 1) / seg;
+    if (smax < 2) return p;
+    p.sg.seg_len = (int32_t)seg;
+    p.sg.seg_max = (int32_t)smax;
+    const size_t mats = (size_t)B * smax * Hv;
+    p.bytes = align_up(mats * d * d * sizeof(float)) + align_up(mats * sizeof(float));
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +405,8 @@ tr_status gdn_replay_impl(const char* fn, const void* q, const void* k, const vo
         return fail(TR_ERR_INVALID_ARG, "%s: q_scale must be finite and > 0", fn);
     if (!state_out) return fail(TR_ERR_INVALID_ARG, "%s: null state_out", fn);
     if (T > 0 && (!q || !k || !v || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
+    if ((((uintptr_t)q | (uintptr_t)k) & 15) != 0)
+        return fail(TR_ERR_INVALID_ARG, "%s: q and k must be 16-byte aligned (rows are read in 16-byte pieces)", fn);
     const bool split = use_split(B, Hv, dv, dt);
     const size_t need = split ? split_workspace_bytes(B, T, Hv, dk, dv) : 0;
     if (noalloc && need > kNoallocScratchBytes)
@@ -396,16 +487,41 @@ tr_status tr_gdn_replay_noalloc(const void* q, const void* k, const void* v,
                            dk, dv, dt, q_scale, state_in, state_out, o, nullptr, 0, true, stream);
 }
 
+size_t tr_gdn_transition_workspace_size(const int32_t* cu_seqlens_host, int32_t B, int32_t Hqk, int32_t Hv,
+                                        int32_t d, tr_dtype dt) {
+    static const char* fn = "tr_gdn_transition_workspace_size";
+    if (!cu_seqlens_host || B < 1) { fail(TR_ERR_INVALID_ARG, "%s: need cu_seqlens_host and B >= 1", fn); return 0; }
+    int32_t max_len = 0;
+    // the device copy is not needed here: pass the host array for the null check
+    if (check_gdn(fn, cu_seqlens_host, cu_seqlens_host, B, cu_seqlens_host[B], Hqk, Hv, d, d, dt, &max_len) != TR_OK)
+        return 0;
+    ok();
+    return transition_plan(cu_seqlens_host, B, Hv, d, max_len).bytes;
+}
+
 tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
                             const int32_t* cu_seqlens_host, const int32_t* cu_seqlens_dev,
                             int32_t B, int32_t T, int32_t Hqk, int32_t Hv, int32_t d,
-                            tr_dtype dt, float* phi_out, float* log_scale_out, void* stream) {
+                            tr_dtype dt, float* phi_out, float* log_scale_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
     static const char* fn = "tr_gdn_transition";
     int32_t max_len = 0;
     const tr_status st = check_gdn(fn, cu_seqlens_host, cu_seqlens_dev, B, T, Hqk, Hv, d, d, dt, &max_len);
     if (st != TR_OK) return st;
     if (!phi_out) return fail(TR_ERR_INVALID_ARG, "%s: null phi_out", fn);
     if (T > 0 && (!k || !g || !beta)) return fail(TR_ERR_INVALID_ARG, "%s: null input pointer", fn);
+    if (((uintptr_t)k & 15) != 0)
+        return fail(TR_ERR_INVALID_ARG, "%s: k must be 16-byte aligned (rows are read in 16-byte pieces)", fn);
+    TransitionPlan plan = transition_plan(cu_seqlens_host, B, Hv, d, max_len);
+    if (plan.bytes > 0) {
+        if (!workspace || workspace_bytes < plan.bytes)
+            return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace ? workspace_bytes : 0,
+                        plan.bytes);
+        if (((uintptr_t)workspace & 15) != 0) return fail(TR_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+        const size_t mats = (size_t)B * plan.sg.seg_max * Hv;
+        plan.sg.phi = (float*)workspace;
+        plan.sg.log = (float*)((unsigned char*)workspace + align_up(mats * d * d * sizeof(float)));
+    }
 
     // The recurrence from S = I with zero values: S_m = I T_{a+1} ... T_m, in fp32 arithmetic
     // for either input type (a product of many operators keeps every rounding it meets).
@@ -416,7 +532,8 @@ tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
     a.log_scale_out = log_scale_out;
     a.uniform_len = 0; a.state_bstride = (int64_t)Hv * d * d;
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_token_f32_bf16in(a, s) : tr::launch_gdn_token_f32(a, s);
+    const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_token_f32_bf16in(a, s, plan.sg)
+                                         : tr::launch_gdn_token_f32(a, s, plan.sg);
     return finish_launch(e, s, fn);
 }
 
@@ -560,49 +677,12 @@ tr_status tr_group_replay(const void* h_tail, const tr_la_weights* w,
         return fail(TR_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes, lay.total);
 
     hipStream_t s = (hipStream_t)stream;
-    unsigned char* ws = (unsigned char*)workspace;
-    bf16* xbuf = (bf16*)(ws + lay.x);
-    bf16* ybuf = (bf16*)(ws + lay.y);
-    bf16* qbuf = (bf16*)(ws + lay.q);
-    bf16* kbuf = (bf16*)(ws + lay.k);
-    bf16* vbuf = (bf16*)(ws + lay.v);
-    bf16* obuf = (bf16*)(ws + lay.o);
-    float* gbuf = (float*)(ws + lay.g);
-    float* bbuf = (float*)(ws + lay.beta);
     std::vector<const tr_la_weights*> wp((size_t)G * L);
     for (size_t i = 0; i < wp.size(); ++i) wp[i] = &w[i];
-
-    const int64_t state_elems = (int64_t)Hv * dv * dk;
-    const void* x_cur = h_tail;
-    for (int32_t li = 0; li < L; ++li) {
-        const bool last = li == L - 1;
-        // projections in front of the recurrence (stride L through the weight table)
-        hipError_t e = layer_inputs(x_cur, wp.data(), L, li, G, n_tokens, d_model, Hqk, Hv, rms_eps, ybuf,
-                                    qbuf, kbuf, vbuf, gbuf, bbuf, s);
-        if (e != hipSuccess) return finish_launch(e, s, fn);
-        // the recurrence from the zero state; the last layer keeps its state only
-        tr::GdnArgs a;
-        a.state_identity = 0;
-        a.log_scale_out = nullptr;
-        a.q = qbuf; a.k = kbuf; a.v = vbuf; a.g = gbuf; a.beta = bbuf;
-        a.cu_seqlens = nullptr; a.uniform_len = n_tokens;
-        a.B = G; a.T = G * n_tokens; a.Hqk = Hqk; a.Hv = Hv; a.dk = dk; a.dv = dv; a.q_scale = 1.0f;
-        a.state_in = nullptr; a.state_out = states_out + (int64_t)li * state_elems;
-        a.state_bstride = (int64_t)L * state_elems;
-        a.o = last ? nullptr : obuf; a.max_len = n_tokens;
-        e = tr::launch_gdn_chunk_bf16(a, s);
-        if (e != hipSuccess) return finish_launch(e, s, fn);
-        if (!last) {
-            e = output_residual(x_cur, obuf, wp.data(), L, li, G, n_tokens, d_model, Hv * dv, xbuf, s);
-            if (e != hipSuccess) return finish_launch(e, s, fn);
-            x_cur = xbuf;
-        }
-        if (debug_sync()) {
-            const tr_status ds = finish_launch(hipSuccess, s, fn);
-            if (ds != TR_OK) return ds;
-        }
-    }
-    return finish_launch(hipSuccess, s, fn);
+    const GroupBuffers buf(workspace, lay);
+    const hipError_t e = group_chain(h_tail, wp.data(), 0, G, L, n_tokens, d_model, Hqk, Hv, dk, dv, rms_eps,
+                                     states_out, buf, s);
+    return finish_launch(e, s, fn);
 }
 
 }  // extern "C"

@@ -96,10 +96,21 @@ struct SplitPlan {
 };
 hipError_t launch_gdn_prep_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
 hipError_t launch_gdn_scan_split_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
+// Segments of the transition product (state_identity, no values, no outputs): with seg_len > 0
+// every sequence of n tokens is cut into max(1, ceil(n / seg_len)) <= seg_max segments that run
+// side by side, each from I; a sequence of several segments writes their products to
+// phi[(b * seg_max + s) * Hv + h] ([dk, dk] each) and log scales to log[(b * seg_max + s) * Hv + h],
+// and a second kernel multiplies them in order into state_out / log_scale_out.
+struct Segments {
+    int32_t seg_len = 0;     // 0: one pass over every whole sequence
+    int32_t seg_max = 1;
+    float* phi = nullptr;
+    float* log = nullptr;
+};
 // Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
-hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream);
+hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream, const Segments& sg = Segments());
 // The same fp32 arithmetic on bf16 inputs (and bf16 outputs).
-hipError_t launch_gdn_token_f32_bf16in(const GdnArgs& a, hipStream_t stream);
+hipError_t launch_gdn_token_f32_bf16in(const GdnArgs& a, hipStream_t stream, const Segments& sg = Segments());
 
 // State algebra and single-token steps (state_ops.hip).
 // out[n] = exp(log_scale[n]) S_c[n] Phi[n] (+ S_hat[n]) for n < N (log_scale may be null); S_c, S_hat, out [N, dv, dk], Phi [N, dk, dk], fp32.

@@ -153,11 +153,22 @@ def gdn_replay_noalloc(q, k, v, g, beta, cu_seqlens, cu_seqlens_dev, state_out, 
     return state_out, o
 
 
+def gdn_transition_workspace_size(cu_seqlens, Hqk: int, Hv: int, d: int, dtype) -> int:
+    """Bytes of workspace tr_gdn_transition needs for this request (0 for none)."""
+    cu = cu_seqlens.to(torch.int32).cpu().contiguous()
+    n = lib().tr_gdn_transition_workspace_size(_ptr(cu), cu.numel() - 1, Hqk, Hv, d, _DT[dtype])
+    msg = lib().tr_last_error().decode()
+    _need(not msg, msg)
+    return int(n)
+
+
 def gdn_transition(k, g, beta, cu_seqlens, cu_seqlens_dev=None, phi_out=None, separate_decay: bool = False,
-                   stream=None):
+                   workspace=None, stream=None):
     """Transition products of the packed spans (tr_gdn_transition): the recurrence from S = I
     with zero values.  k [T, Hqk, d] bf16 or fp32; g, beta [T, Hv] fp32.  Returns Phi
-    [B, Hv, d, d], or with separate_decay (phi, log_scale [B, Hv]) where Phi = exp(log_scale) phi."""
+    [B, Hv, d, d], or with separate_decay (phi, log_scale [B, Hv]) where Phi = exp(log_scale) phi.
+    workspace: a uint8 device tensor of at least gdn_transition_workspace_size() bytes, or None
+    to allocate one when the request needs it."""
     _need(k.is_cuda and g.is_cuda and beta.is_cuda, "inputs must be on the GPU")
     _need(k.dtype in _DT and g.dtype == torch.float32 and beta.dtype == torch.float32, "dtypes")
     for t in (k, g, beta):
@@ -175,8 +186,17 @@ def gdn_transition(k, g, beta, cu_seqlens, cu_seqlens_dev=None, phi_out=None, se
     _need(phi_out.is_cuda and phi_out.dtype == torch.float32 and phi_out.is_contiguous()
           and tuple(phi_out.shape) == (B, Hv, d, d), "phi_out must be [B, Hv, d, d] fp32")
     log_scale = torch.empty((B, Hv), dtype=torch.float32, device=k.device) if separate_decay else None
+    if workspace is None:
+        need = lib().tr_gdn_transition_workspace_size(_ptr(cu), B, Hqk, Hv, d, _DT[k.dtype])
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
     check(lib().tr_gdn_transition(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu), _ptr(cu_seqlens_dev),
-                                  B, T, Hqk, Hv, d, _DT[k.dtype], _ptr(phi_out), _ptr(log_scale), _stream(stream)))
+                                  B, T, Hqk, Hv, d, _DT[k.dtype], _ptr(phi_out), _ptr(log_scale),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
     return (phi_out, log_scale) if separate_decay else phi_out
 
 

@@ -87,6 +87,7 @@ def call_gdn(**over):
     (dict(s_out=None), 1),
     (dict(cu_d=None), 1),
     (dict(T=10), 1),                       # cu[B] != T
+    (dict(k=ctypes.c_void_p(0x1008)), 1),  # not 16-byte aligned
 ])
 def test_gdn_rejects_bad_arguments(over, status):
     st, msg = call_gdn(**over)
@@ -139,21 +140,45 @@ def test_gdn_rejects_bad_cu_seqlens():
 def call_transition(**over):
     cu = (ctypes.c_int32 * 3)(0, 5, 9)
     args = dict(k=FAKE, g=FAKE, beta=FAKE, cu_h=ctypes.cast(cu, ctypes.c_void_p), cu_d=FAKE,
-                B=2, T=9, Hqk=2, Hv=4, d=128, dt=0, phi=FAKE)
+                B=2, T=9, Hqk=2, Hv=4, d=128, dt=0, phi=FAKE, ws=None, ws_bytes=0)
     args.update(over)
     lib = L.lib()
     st = lib.tr_gdn_transition(args["k"], args["g"], args["beta"], args["cu_h"], args["cu_d"], args["B"], args["T"],
-                               args["Hqk"], args["Hv"], args["d"], args["dt"], args["phi"], None, None)
+                               args["Hqk"], args["Hv"], args["d"], args["dt"], args["phi"], None,
+                               args["ws"], args["ws_bytes"], None)
     return st, lib.tr_last_error().decode()
+
+
+LONG_SPAN = (ctypes.c_int32 * 2)(0, 1639)
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(B=0), 1), (dict(Hv=3), 1), (dict(d=96), 2), (dict(dt=5), 1), (dict(k=None), 1),
-    (dict(phi=None), 1), (dict(cu_d=None), 1), (dict(T=8), 1),
+    (dict(phi=None), 1), (dict(cu_d=None), 1), (dict(T=8), 1), (dict(k=ctypes.c_void_p(0x1002)), 1),
+    # one long span with few heads is cut into segments, which need the workspace
+    (dict(cu_h=ctypes.cast(LONG_SPAN, ctypes.c_void_p), B=1, T=1639), 3),
+    (dict(cu_h=ctypes.cast(LONG_SPAN, ctypes.c_void_p), B=1, T=1639, ws=FAKE, ws_bytes=4096), 3),
+    (dict(cu_h=ctypes.cast(LONG_SPAN, ctypes.c_void_p), B=1, T=1639, ws=ctypes.c_void_p(0x1004), ws_bytes=1 << 30), 1),
 ])
 def test_transition_rejects_bad_arguments(over, status):
     st, msg = call_transition(**over)
     assert st == status and "tr_gdn_transition" in msg
+
+
+def test_transition_workspace_size():
+    lib = L.lib()
+    # a single 1,639-token span over 16 heads: cut into segments, one fp32 d x d product each
+    n = lib.tr_gdn_transition_workspace_size(ctypes.cast(LONG_SPAN, ctypes.c_void_p), 1, 16, 16, 128, 0)
+    assert lib.tr_last_error().decode() == ""
+    assert n >= 2 * 16 * 128 * 128 * 4
+    # many sequences already fill the chip: no segments, no workspace
+    many = (ctypes.c_int32 * 65)(*[100 * i for i in range(65)])
+    assert lib.tr_gdn_transition_workspace_size(ctypes.cast(many, ctypes.c_void_p), 64, 16, 32, 128, 0) == 0
+    # a span of one minimal segment is not cut
+    short = (ctypes.c_int32 * 2)(0, 128)
+    assert lib.tr_gdn_transition_workspace_size(ctypes.cast(short, ctypes.c_void_p), 1, 1, 1, 128, 0) == 0
+    assert lib.tr_gdn_transition_workspace_size(None, 1, 16, 16, 128, 0) == 0
+    assert "tr_gdn_transition_workspace_size" in lib.tr_last_error().decode()
 
 
 def test_state_compose_rejects_bad_arguments():

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 import synthetic
-from linear_attention_state_amd import gdn_replay, gdn_transition, state_compose, tail_seqlens
+from linear_attention_state_amd import (gdn_replay, gdn_transition, gdn_transition_workspace_size, state_compose,
+                                        tail_seqlens)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +76,27 @@ def test_transition_matches_oracle(d, dtype, tol):
     for b in range(len(lens)):
         for h in range(4):
             assert rel(np.exp(np64(ls[b, h])) * np64(psi[b, h]), ref[b, h]) <= tol
+
+
+@pytest.mark.parametrize("lens,Hv,min_segments", [([4000], 1, 16), ([1639, 900, 0, 1639], 4, 2)])
+def test_transition_in_segments(lens, Hv, min_segments):
+    # Few (sequence, head) pairs: every span is cut into segments that run side by side and are
+    # multiplied in order.  One 4,000-token span on one head takes the most segments (16, of
+    # 250 tokens); the packed case mixes several segments per span with an empty span.
+    d = 128
+    inp = synthetic.gdn_inputs(lens, 1, Hv, d, d, seed=17)
+    n_ws = gdn_transition_workspace_size(inp.cu_seqlens, 1, Hv, d, torch.bfloat16)
+    assert n_ws >= min_segments * len(lens) * Hv * d * d * 4
+    dev = inp.to("cuda")
+    psi, ls = gdn_transition(dev.k, dev.g, dev.beta, inp.cu_seqlens, separate_decay=True)
+    torch.cuda.synchronize()
+    psi_ref, ls_ref = oracle_phi_separated(np64(inp.k), np64(inp.g), np64(inp.beta), inp.cu_seqlens.numpy(), d)
+    worst = max(rel(np64(psi[b, h]), psi_ref[b, h]) for b in range(len(lens)) for h in range(Hv))
+    print("segments %s x %d heads: worst psi err %.3e" % (lens, Hv, worst), flush=True)
+    assert worst <= PHI_TOL
+    np.testing.assert_allclose(np64(ls), ls_ref, rtol=1e-5, atol=1e-5)
+    if 0 in lens:
+        assert np.array_equal(np64(psi[lens.index(0), 0]), np.eye(d))
 
 
 def test_compose_matches_definition():
