@@ -31,8 +31,9 @@
 //   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L: the diagonal
 //       blocks transposed in fp32, the off-diagonal blocks row-major in bf16 (LDS);
 //       stage Q
-//   P2  A = (I + L)^{-1} in two steps: each wave inverts one 16x16 diagonal block in fp32 on
-//       MFMA, as (I - L)(I + L^2)(I + L^4)(I + L^8) (the block is nilpotent); after a barrier,
+//   P2  A = (I + L)^{-1} in two steps: each wave inverts one 16x16 diagonal block, as
+//       (I - L)(I + L^2)(I + L^4)(I + L^8) (the block is nilpotent), each product from bf16
+//       hi / lo splits on 16x16x16 MFMA with fp32 accumulation; after a barrier,
 //       wave j forms block column j of A - I by 16x16x16 MFMA merges.  The Q K^T tiles are
 //       spread over the waves (1, 3, 3, 3: wave 0 has the longest merge chain)
 //   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
@@ -425,24 +426,26 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         lds_barrier();
 
         // ------------------- P2: A = (I + L)^{-1}, two steps; Q K^T tiles on every wave
-        // Step 1: the diagonal blocks D_b = (I + L_bb)^{-1}, block b on wave b % NW, in fp32 on
-        // MFMA: L_bb is strictly lower triangular (nilpotent), so
-        //     D_b = (I - L)(I + L^2)(I + L^4)(I + L^8).
+        // Step 1: the diagonal blocks D_b = (I + L_bb)^{-1}, block b on wave b % NW: L_bb is
+        // strictly lower triangular (nilpotent), so
+        //     D_b = (I - L)(I + L^2)(I + L^4)(I + L^8),
+        // each product from hi / lo bf16 splits (about 2^-16 relative, far below the bf16
+        // rounding that every later use of D_b applies).
         for (int b = wave; b < 4; b += NW) {
             const int base = 16 * b;
             f32x4 Lr, La;                                   // L_bb in row and accumulator layout
 #pragma unroll
             for (int e = 0; e < 4; ++e) Lr[e] = sm.lw.l.Ld[b][4 * g4 + e][l16];
             La = *reinterpret_cast<const f32x4*>(&sm.lw.l.Ld[b][l16][4 * g4]);
-            const f32x4 L2a = mm16f(Lr, La, zero4()), L2r = mm16f(La, Lr, zero4());
-            const f32x4 L4a = mm16f(L2r, L2a, zero4()), L4r = mm16f(L2a, L2r, zero4());
-            const f32x4 L8r = mm16f(L4a, L4r, zero4());
+            const f32x4 L2a = mm16x3(Lr, La, zero4()), L2r = mm16x3(La, Lr, zero4());
+            const f32x4 L4a = mm16x3(L2r, L2a, zero4()), L4r = mm16x3(L2a, L2r, zero4());
+            const f32x4 L8r = mm16x3(L4a, L4r, zero4());
             f32x4 D;                                        // I - L, accumulator layout
 #pragma unroll
             for (int j = 0; j < 4; ++j) D[j] = (4 * g4 + j == l16 ? 1.f : 0.f) - La[j];
-            D = mm16f(L2r, D, D);
-            D = mm16f(L4r, D, D);
-            D = mm16f(L8r, D, D);                           // lane (n, g): D[4g + j][n]
+            D = mm16x3(L2r, D, D);
+            D = mm16x3(L4r, D, D);
+            D = mm16x3(L8r, D, D);                          // lane (n, g): D[4g + j][n]
             const float bn = sm.bt[base + l16], bgn = sm.bg[base + l16];
             bf16x4 ad;
 #pragma unroll

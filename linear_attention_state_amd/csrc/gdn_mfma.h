@@ -29,15 +29,28 @@ __device__ __forceinline__ f32x4 mma16k32(const bf16x8& a, const bf16x8& b, cons
 __device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// fp32 16x16 product on 16x16x4 fp32 MFMA.  X in row layout (lane (m, g = l / 16) holds
-// X[m][4g .. 4g+3]) times Y in accumulator layout (lane (n, g) holds Y[4g .. 4g+3][n]),
-// plus C, gives the accumulator layout; step s pairs contraction index 4g + s on both sides.
-// With the operands swapped (Y's registers as X, X's as Y) the same call gives the product
-// transposed, i.e. in row layout.
-__device__ __forceinline__ f32x4 mm16f(const f32x4& xrow, const f32x4& yacc, f32x4 c) {
+// 16x16 products in two operand layouts: X in row layout (lane (m, g = l / 16) holds
+// X[m][4g .. 4g+3]) and Y in accumulator layout (lane (n, g) holds Y[4g .. 4g+3][n]); X Y + C
+// comes out in the accumulator layout.  With the operands swapped (Y's registers as X, X's as
+// Y) the same call gives the product transposed, i.e. in row layout.
+// The product is formed from bf16 hi / lo splits of both operands on 16x16x16 bf16 MFMA (the
+// A and B operand layouts of that instruction are the row and accumulator layouts):
+// X Y ~ Xhi Yhi + Xhi Ylo + Xlo Yhi, leaving out Xlo Ylo (about 2^-16 of |X| |Y| per term),
+// small terms first.  Three 16x16x16 products instead of four fp32 16x16x4 ones.
+__device__ __forceinline__ void split_bf4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[s], yacc[s], c, 0, 0, 0);
-    return c;
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (bf16)x[i];
+        lo[i] = (bf16)(x[i] - (float)hi[i]);
+    }
+}
+__device__ __forceinline__ f32x4 mm16x3(const f32x4& xrow, const f32x4& yacc, f32x4 c) {
+    bf16x4 xh, xl, yh, yl;
+    split_bf4(xrow, xh, xl);
+    split_bf4(yacc, yh, yl);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, yh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, yl, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, yh, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
