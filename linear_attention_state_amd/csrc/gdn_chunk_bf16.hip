@@ -28,14 +28,14 @@
 // x 32 dv columns).  Per chunk:
 //   P0  stage K (loaded one chunk ahead, with g and beta); gate cumsum and the exp2 tables;
 //       issue this chunk's Q and V loads and the next chunk's K, g, beta loads
-//   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L: the diagonal
-//       blocks transposed in fp32, the off-diagonal blocks row-major in bf16 (LDS);
-//       stage Q
-//   P2  A = (I + L)^{-1} in two steps: each wave inverts one 16x16 diagonal block, as
-//       (I - L)(I + L^2)(I + L^4)(I + L^8) (the block is nilpotent), each product from bf16
-//       hi / lo splits on 16x16x16 MFMA with fp32 accumulation; after a barrier,
-//       wave j forms block column j of A - I by 16x16x16 MFMA merges.  The Q K^T tiles are
-//       spread over the waves (1, 3, 3, 3: wave 0 has the longest merge chain)
+//   P1  K K^T lower 16x16 tiles on 16x16x32 MFMA, masked and decayed into L: the
+//       off-diagonal blocks row-major in bf16 (LDS); the wave that forms a diagonal block
+//       inverts it in registers at once, as (I - L)(I + L^2)(I + L^4)(I + L^8) (the block
+//       is nilpotent), each product from bf16 hi / lo splits on 16x16x16 MFMA with fp32
+//       accumulation; stage Q
+//   P2  the rest of A = (I + L)^{-1}: wave j forms block column j of A - I by 16x16x16
+//       MFMA merges.  The Q K^T tiles are spread over the waves (1, 3, 3, 3: wave 0 has the
+//       longest merge chain)
 //   P3  U0 (own value columns, V read straight from HBM in operand order) and -W (to LDS);
 //       K^T operands come from the row-major K tile through LDS transpose reads
 //   P4  P (bf16 hi/lo) to LDS, over the dead (A - I) tiles
@@ -97,7 +97,6 @@ struct Smem {
     bf16 Q[CH][DK + 8];         // query rows
     union {
         struct {
-            float Ld[4][16][20];    // diagonal 16x16 blocks of L, transposed (Ld[b][i][t] = L_ti), fp32
             bf16 Lb[CH][RS_T];      // L row-major in bf16 (off-diagonal blocks used): P1 .. P2
         } l;
         bf16 Wn[CH][DK + 8];    // -W rows: P3 .. P5
@@ -344,20 +343,54 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         lds_barrier();
 
         // ------------------------------------------------------------- P1: K K^T -> L
-        // Diagonal tiles come out with lane (n, q) holding rows 4q..4q+3 of column n (the layout
-        // the inverse reads as fp32); off-diagonal tiles are formed transposed (operands
-        // swapped), so lane (m, q) holds row m, columns 4q..4q+3, stored as bf16 rows for the
-        // merges' A operands.
-        auto l_diag = [&](int b, const f32x4& acc) {
-            const int ci = 16 * b + l16;
-            const float gi = sm.g2[ci];
-            const int r0 = 16 * b + 4 * g4;
+        // Diagonal tiles come out with lane (n, q) holding rows 4q..4q+3 of column n; the wave
+        // that forms one inverts it at once (below).  Off-diagonal tiles are formed transposed
+        // (operands swapped), so lane (m, q) holds row m, columns 4q..4q+3, stored as bf16
+        // rows for the merges' A operands.
+        //
+        // The diagonal blocks D_b = (I + L_bb)^{-1}: L_bb is strictly lower triangular
+        // (nilpotent), so
+        //     D_b = (I - L)(I + L^2)(I + L^4)(I + L^8),
+        // each product from hi / lo bf16 splits (about 2^-16 relative, far below the bf16
+        // rounding that every later use of D_b applies).  The raw tile K_b K_b^T is symmetric,
+        // so the accumulator that holds it in accumulator layout (lane (n, q): rows 4q..4q+3
+        // of column n) also holds it in row layout (lane (m, q): row m, columns 4q..4q+3):
+        // both layouts of L_bb come from one product, with the mask and decay applied per
+        // layout.
+        auto invert_diag = [&](int b, const f32x4& raw) {
+            const int base = 16 * b;
+            const int ci = base + l16;                    // this lane's column (acc) / row (row layout)
+            const int r0 = base + 4 * g4;                 // rows (acc) / columns (row layout) r0..r0+3
+            const float gi = sm.g2[ci], bi = sm.bt[ci];
             const f32x4 gt = tab4(sm.g2, r0), bt = tab4(sm.bt, r0);
-            f32x4 lv;
+            f32x4 La, Lr;                                 // L_bb in accumulator and row layout
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                lv[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * acc[j] : 0.f;
-            *reinterpret_cast<f32x4*>(&sm.lw.l.Ld[b][l16][4 * g4]) = lv;
+            for (int j = 0; j < 4; ++j) {
+                La[j] = (ci < r0 + j) ? bt[j] * __builtin_amdgcn_exp2f(gt[j] - gi) * raw[j] : 0.f;
+                Lr[j] = (ci > r0 + j) ? bi * __builtin_amdgcn_exp2f(gi - gt[j]) * raw[j] : 0.f;
+            }
+            const f32x4 L2a = mm16x3(Lr, La, zero4()), L2r = mm16x3(La, Lr, zero4());
+            const f32x4 L4a = mm16x3(L2r, L2a, zero4()), L4r = mm16x3(L2a, L2r, zero4());
+            const f32x4 L8r = mm16x3(L4a, L4r, zero4());
+            f32x4 D;                                      // I - L, accumulator layout
+#pragma unroll
+            for (int j = 0; j < 4; ++j) D[j] = (r0 + j == ci ? 1.f : 0.f) - La[j];
+            D = mm16x3(L2r, D, D);
+            D = mm16x3(L4r, D, D);
+            D = mm16x3(L8r, D, D);                        // lane (n, g): D[4g + j][n]
+            const float bgn = sm.bg[ci];
+            bf16x4 ad;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g4 + j;
+                ad[j] = (bf16)D[j];
+                const float nn = r > l16 ? D[j] : 0.f;    // strictly lower part: A - I
+                sm.np.n.Nb[base + r][base + l16] = (bf16)(nn * bi);
+                sm.np.n.Nbg[base + r][base + l16] = (bf16)(nn * bgn);
+            }
+            *reinterpret_cast<bf16x4*>(&sm.AdT[b][l16][4 * g4]) = ad;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.Ad[b][4 * g4 + j][l16] = ad[j];
         };
         auto l_off = [&](int rb, int cb, const f32x4& acc) {
             const int t = 16 * rb + l16;                  // row (later token)
@@ -395,7 +428,7 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                 a1 = mma16k32(x1, y1, a1);
                 a2 = mma16k32(x2, y2, a2);
             }
-            l_diag(wave, ad);
+            invert_diag(wave, ad);
             l_off(r1, c1, a1);
             l_off(r2, c2, a2);
         } else {
@@ -413,7 +446,7 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                     for (int s = 0; s < DK / 32; ++s)
                         acc = mma16k32(*reinterpret_cast<const bf16x8*>(xrow + 32 * s + 8 * g4),
                                        *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g4), acc);
-                    if (diag) l_diag(rb, acc);
+                    if (diag) invert_diag(rb, acc);
                     else l_off(rb, cb, acc);
                 }
             }
@@ -425,44 +458,8 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
         }
         lds_barrier();
 
-        // ------------------- P2: A = (I + L)^{-1}, two steps; Q K^T tiles on every wave
-        // Step 1: the diagonal blocks D_b = (I + L_bb)^{-1}, block b on wave b % NW: L_bb is
-        // strictly lower triangular (nilpotent), so
-        //     D_b = (I - L)(I + L^2)(I + L^4)(I + L^8),
-        // each product from hi / lo bf16 splits (about 2^-16 relative, far below the bf16
-        // rounding that every later use of D_b applies).
-        for (int b = wave; b < 4; b += NW) {
-            const int base = 16 * b;
-            f32x4 Lr, La;                                   // L_bb in row and accumulator layout
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Lr[e] = sm.lw.l.Ld[b][4 * g4 + e][l16];
-            La = *reinterpret_cast<const f32x4*>(&sm.lw.l.Ld[b][l16][4 * g4]);
-            const f32x4 L2a = mm16x3(Lr, La, zero4()), L2r = mm16x3(La, Lr, zero4());
-            const f32x4 L4a = mm16x3(L2r, L2a, zero4()), L4r = mm16x3(L2a, L2r, zero4());
-            const f32x4 L8r = mm16x3(L4a, L4r, zero4());
-            f32x4 D;                                        // I - L, accumulator layout
-#pragma unroll
-            for (int j = 0; j < 4; ++j) D[j] = (4 * g4 + j == l16 ? 1.f : 0.f) - La[j];
-            D = mm16x3(L2r, D, D);
-            D = mm16x3(L4r, D, D);
-            D = mm16x3(L8r, D, D);                          // lane (n, g): D[4g + j][n]
-            const float bn = sm.bt[base + l16], bgn = sm.bg[base + l16];
-            bf16x4 ad;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * g4 + j;
-                ad[j] = (bf16)D[j];
-                const float nn = r > l16 ? D[j] : 0.f;      // strictly lower part: A - I
-                sm.np.n.Nb[base + r][base + l16] = (bf16)(nn * bn);
-                sm.np.n.Nbg[base + r][base + l16] = (bf16)(nn * bgn);
-            }
-            *reinterpret_cast<bf16x4*>(&sm.AdT[b][l16][4 * g4]) = ad;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sm.Ad[b][4 * g4 + j][l16] = ad[j];
-        }
-        lds_barrier();
-
-        // Step 2: off-diagonal blocks, one block column per wave:
+        // ------------------- P2: A = (I + L)^{-1} off the diagonal; Q K^T tiles on every wave
+        // Off-diagonal blocks, one block column per wave:
         // A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj on 16x16x16 bf16 MFMA.  16x16x16 layouts: the A
         // operand lane (m = l % 16, q = l / 16) holds row m, k = 4q..4q+3; the B operand and the
         // accumulator hold rows 4q..4q+3 of column l % 16, so a result feeds the next product's
