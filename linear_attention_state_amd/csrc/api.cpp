@@ -283,7 +283,8 @@ tr_status check_gdn(const char* fn, const int32_t* cu_seqlens_host, const int32_
 
 // Schedule of the bf16 recurrence (tr_gdn_set_schedule).  The split schedule is chosen
 // automatically when the fused one would leave most of the chip idle: at most
-// kSplitMaxWaves state-scan waves (32 value columns each).
+// kSplitMaxWaves 32-column state slices in all, i.e. two rounds of the scan's workgroups (one
+// pair of waves per slice, one workgroup per CU).
 std::atomic<int> g_schedule{TR_SCHEDULE_AUTO};
 constexpr int64_t kSplitMaxWaves = 512;
 
