@@ -113,10 +113,10 @@ tr_status tr_tail_seqlens(const int64_t* m_host, int32_t B, int32_t r_num, int32
  *   stream      hipStream_t to enqueue on
  * Schedules (bf16): the fused schedule runs one workgroup per (sequence, value head) and
  * needs no workspace.  With few heads that leaves most of the chip idle, so the split
- * schedule (default for at most 512 / (dv / 32) heads in all) first runs every chunk's
+ * schedule (default for at most 256 / (dv / 32) heads in all) first runs every chunk's
  * state-free part in parallel -- gate cumsum, K K^T, (I + L)^{-1}, W, U0, Q K^T -- into the
  * workspace, then the state scan with each state split along dv across workgroups (rows of S
- * evolve independently, section 2.3).  Both give the same results to within rounding.
+ * evolve independently, section 2.3).  Both schedules give the same bits.
  * Supported: dk, dv in {64, 128}.  Empty sequences copy state_in (or write zeros).
  * Errors: TR_ERR_INVALID_ARG (sizes, pointers, cu_seqlens), TR_ERR_UNSUPPORTED (head
  *   dims), TR_ERR_WORKSPACE (workspace NULL or smaller than needed), TR_ERR_HIP.

@@ -113,6 +113,8 @@ def test_gdn_schedule_and_workspace_query():
         assert _ws_size([0, 5, 9], 2, Hv=8) == 2 * n1
         assert _ws_size([0, 5, 9], 2, dt=1) == 0            # fp32 inputs: token path, no workspace
         assert _ws_size([0, 5, 9], 2, Hv=128) == 0          # many heads: fused
+        assert _ws_size([0, 5, 9], 2, Hv=32) > 0            # 256 state slices of 32 columns: split
+        assert _ws_size([0, 5, 9], 2, Hv=64) == 0           # 512: fused
         assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_FUSED) == C.TR_OK
         assert _ws_size([0, 5, 9], 2) == 0
         assert lib.tr_gdn_set_schedule(C.TR_SCHEDULE_SPLIT) == C.TR_OK
