@@ -18,8 +18,8 @@ Contents
   ``chain.py``.
 * :func:`round_bf16` / :func:`round_f32` -- the rounding points of the contract.
 
-Functions whose result has no pin other than this package itself are listed as
-"parity unpinned" in ``chain.py``'s header.
+Every function here is pinned by tests/test_oracle.py or tests/test_oracle_group.py
+to closed forms, invariants or library routines outside this package.
 """
 from __future__ import annotations
 

@@ -27,9 +27,11 @@ library stores a tensor in that type; between them everything is float64.
 
 Pins: tests/test_oracle_group.py checks the chain against a constructed case with
 a closed-form answer (one-hot keys and saturated gates give exact key-value
-recall), RMSNorm / L2-norm invariants, residual pass-through, scale invariance of
-the first layer, and gate ranges.  The bf16 GEMM inputs themselves are parity
-unpinned beyond numpy's float64 matmul.
+recall), the projections on exact weights whose every output has a closed form
+(orientation, head order, per-head L2 norm, q scale, gate maps against numpy's
+logaddexp and scipy's expit), RMSNorm with a gain in closed form, RMSNorm / L2-norm
+invariants, residual pass-through, scale invariance of the first layer, and gate
+ranges.  Random-weight projections are otherwise numpy's float64 matmul.
 """
 from __future__ import annotations
 

@@ -107,3 +107,47 @@ def test_first_layer_is_scale_invariant():
     S_a = og.group(h, ws, Hqk, Hv, dk, dv)
     S_b = og.group(2.0 * h, ws, Hqk, Hv, dk, dv)
     assert np.linalg.norm(S_a - S_b) <= 1e-2 * np.linalg.norm(S_a)
+
+
+def test_projection_values_on_exact_weights():
+    # Weights whose rows pick single hidden coordinates (or the pair (3, 4) of them), so every
+    # projected value has a closed form: pins the [out, in] orientation of each weight, the
+    # order of the q heads then the k heads, the per-head L2 norm, the q scale dk^-1/2, the
+    # head-major split of v, and the gate maps against independent library routines.
+    from scipy.special import expit
+    d, Hqk, Hv, dk, dv = 16, 2, 2, 4, 4
+    y = np.array([[1.0, -2.0, 0.5, 4.0, -1.0, 3.0, 2.0, -0.25, 0.75, 1.5, -3.0, 0.125, 2.5, -0.5, 1.25, -4.0],
+                  [0.5, 1.0, -1.5, 2.0, 3.0, -0.75, 0.25, 1.0, -2.0, 0.5, 1.0, -1.0, 0.375, 2.0, -2.5, 1.0]])
+    assert np.array_equal(oracle.round_bf16(y), y)
+    # q head h and k head h: 3 y[a] + 4 y[b] in column 0, y[c] in column 1 (others 0)
+    picks = {("q", 0): (0, 1, 2), ("q", 1): (3, 4, 5), ("k", 0): (6, 7, 8), ("k", 1): (9, 10, 11)}
+    w_qk = np.zeros((2 * Hqk * dk, d))
+    for (kind, h), (a, b, c) in picks.items():
+        row = (0 if kind == "q" else Hqk * dk) + h * dk
+        w_qk[row, a], w_qk[row, b], w_qk[row + 1, c] = 3.0, 4.0, 1.0
+    perm = np.array([5, 2, 7, 0, 12, 15, 1, 9])          # v output j reads y[perm[j]]
+    w_v = np.zeros((Hv * dv, d)); w_v[np.arange(Hv * dv), perm] = 1.0
+    w_a = np.zeros((Hv, d)); w_a[0, 3], w_a[1, 10] = 1.0, 0.5      # za = (y3, y10 / 2)
+    w_b = np.zeros((Hv, d)); w_b[0, 13], w_b[1, 14] = 2.0, 1.0     # zb = (2 y13, y14)
+    q, k, v, g, beta = og.project(y, dict(w_qk=w_qk, w_v=w_v, w_a=w_a, w_b=w_b), Hqk, Hv, dk, dv)
+    for t in range(2):
+        for (kind, h), (a, b, c) in picks.items():
+            x0, x1 = 3.0 * y[t, a] + 4.0 * y[t, b], y[t, c]
+            nrm = np.sqrt(x0 * x0 + x1 * x1 + og.L2_EPS)
+            scale = dk ** -0.5 if kind == "q" else 1.0
+            expect = oracle.round_bf16(np.array([x0, x1, 0.0, 0.0]) / nrm * scale)
+            got = (q if kind == "q" else k)[t, h]
+            np.testing.assert_array_equal(got, expect)
+        np.testing.assert_array_equal(v[t].reshape(-1), y[t, perm])
+        za = np.array([y[t, 3], y[t, 10] / 2.0])
+        zb = np.array([2.0 * y[t, 13], y[t, 14]])
+        np.testing.assert_allclose(g[t], -np.logaddexp(0.0, za), rtol=1e-7)
+        np.testing.assert_allclose(beta[t], expit(zb), rtol=1e-7)
+
+
+def test_rmsnorm_closed_form():
+    # RMS of (3, 4, 0, 0) is 2.5; the gain multiplies after the normalisation
+    x = np.array([[3.0, 4.0, 0.0, 0.0]])
+    gain = np.array([1.0, 2.0, 3.0, 4.0])
+    y = og.rmsnorm(x, gain, 0.0)
+    np.testing.assert_allclose(y, [[1.2, 3.2, 0.0, 0.0]], rtol=1e-15)

@@ -102,6 +102,14 @@ CHAIN_MUTANTS = {
     "no_rmsnorm": ("y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)", "y = x"),
     "gate_sign": ("g = round_f32(-softplus(za))", "g = round_f32(softplus(za))"),
     "no_key_norm": ("k = round_bf16(l2norm_heads(qk[:, Hqk * dk:], Hqk, dk))", "k = round_bf16(qk[:, Hqk * dk:].reshape(-1, Hqk, dk))"),
+    "q_scale_dropped": ("q = round_bf16(l2norm_heads(qk[:, : Hqk * dk], Hqk, dk) * dk ** -0.5)",
+                        "q = round_bf16(l2norm_heads(qk[:, : Hqk * dk], Hqk, dk))"),
+    "gate_weights_swapped": ('za = y @ np.asarray(w["w_a"], dtype=np.float64).T\n    zb = y @ np.asarray(w["w_b"], dtype=np.float64).T',
+                             'za = y @ np.asarray(w["w_b"], dtype=np.float64).T\n    zb = y @ np.asarray(w["w_a"], dtype=np.float64).T'),
+    "beta_softplus": ("beta = round_f32(sigmoid(zb))", "beta = round_f32(softplus(zb))"),
+    "rms_gain_ignored": ("        y = y * np.asarray(gain, dtype=np.float64)", "        y = y * 1.0"),
+    "heads_interleaved": ("    xs = x.reshape(x.shape[0], n_heads, d_head)",
+                          "    xs = x.reshape(x.shape[0], d_head, n_heads).transpose(0, 2, 1)"),
     "states_from_previous_layer": ("S, o = gdn(q, k, v, g, beta, cu, q_scale=1.0, want_o=not last)",
                                    "S, o = gdn(q, k, v, g, beta, cu, q_scale=1.0, want_o=not last, "
                                    "state_in=states[gi, li - 1:li] if li else None)"),
