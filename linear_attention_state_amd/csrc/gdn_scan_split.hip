@@ -9,8 +9,9 @@
 // q_t.k_i (hi / lo), U0 = A diag(beta) V and the gate tables, as MFMA operand fragments.
 // Here a workgroup of two waves owns 32 value columns of one (sequence, value head), and the
 // pair splits each chunk's products between them.  Wave h forms U' = U0 + (-W) S^T and
-// Y = Q S^T for token rows [32 h, 32 h + 32) over all of dk, then the waves swap their U'
-// halves through LDS; wave h stores the outputs of its rows,
+// Y = Q S^T for token rows [32 h, 32 h + 32) over all of dk, splits its rows' U' and
+// U' diag(dec) into the bf16 hi / lo operands of the next products and swaps them with its
+// partner through LDS; wave h stores the outputs of its rows,
 //     O  = diag(q_scale e^gamma) Y + P U'      (stored as 32-bit words of two value columns),
 // and updates its half of the state tiles (dk rows [dk h / 2, dk (h + 1) / 2)),
 //     S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K,
@@ -95,11 +96,13 @@ struct Stage {
     float U0[2 * 64 * 16];        // U0 accumulators of this workgroup's 32 columns (row tiles 0, 1)
     float tab[4][CH];             // beta, q_scale e^gamma, e^{gamma_last - gamma}, e^gamma
 };
-// What the two waves of a pair hand each other: U' of a row tile (fp32 accumulators) and the
-// bf16 state operands of a half of the dk rows.
+// What the two waves of a pair hand each other: the bf16 hi / lo operands of their U' rows --
+// of U' diag(dec) for the state update (both waves) and of U' for P U' (wave 0 to wave 1) --
+// and the bf16 state operands of a half of the dk rows.
 template <int DK>
 struct Swap {
-    float U[2][64 * 16];
+    bf16 D[2][4 * 64 * 8];        // [wave][(k-step 0/1 of its rows) x (hi, lo)] fragments
+    bf16 Uo[4 * 64 * 8];          // wave 0's U' hi / lo for k-steps 0, 1
     bf16 Sb[2][(DK / 32) * 64 * 8];
 };
 
@@ -261,7 +264,7 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
             const Stage<DK>& S = st[c & 1];
 
             // U' = U0 + (-W) S^T and Y = Q S^T for row tile h, k-steps in order
-            f32x16 U[2], Y;
+            f32x16 U[2], Y;     // U[h] only: the partner's rows arrive as split operands
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(&S.U0[(h * 64 + lane) * 16 + 4 * q4]);
@@ -274,25 +277,45 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                 U[h] = mma32(fw[s], sb[s], U[h]);
                 if (WITH_O) Y = mma32(fq[s], sb[s], Y);
             }
-            // swap the U' row tiles
+            // this wave's rows: U' hi / lo for P U' (k-steps 2h, 2h + 1) and U' diag(dec) hi / lo
+            // for the state update, handed to the partner (each split once, by the wave that
+            // holds the rows)
+            bf16x8 uh[4], ul[4], dh[4], dl[4];
+            if (WITH_O) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *reinterpret_cast<f32x4*>(&sw.U[h][lane * 16 + 4 * q4]) =
-                    f32x4{U[h][4 * q4], U[h][4 * q4 + 1], U[h][4 * q4 + 2], U[h][4 * q4 + 3]};
+                for (int s = 2 * h; s < 2 * h + 2; ++s) acc_to_b_split(U[h], s, uh[s], ul[s]);
+            }
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 d = *reinterpret_cast<const f32x4*>(&S.tab[2][32 * h + 8 * j4 + 4 * h2]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) U[h][4 * j4 + i] *= d[i];
+            }
+#pragma unroll
+            for (int s = 2 * h; s < 2 * h + 2; ++s) {
+                acc_to_b_split(U[h], s, dh[s], dl[s]);
+                *reinterpret_cast<bf16x8*>(&sw.D[h][((2 * (s - 2 * h)) * 64 + lane) * 8]) = dh[s];
+                *reinterpret_cast<bf16x8*>(&sw.D[h][((2 * (s - 2 * h) + 1) * 64 + lane) * 8]) = dl[s];
+                if (WITH_O && h == 0) {
+                    *reinterpret_cast<bf16x8*>(&sw.Uo[((2 * s) * 64 + lane) * 8]) = uh[s];
+                    *reinterpret_cast<bf16x8*>(&sw.Uo[((2 * s + 1) * 64 + lane) * 8]) = ul[s];
+                }
+            }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&sw.U[1 - h][lane * 16 + 4 * q4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) U[1 - h][4 * q4 + e] = x[e];
+            for (int s = 2 * (1 - h); s < 2 * (1 - h) + 2; ++s) {
+                dh[s] = frag(sw.D[1 - h], 2 * (s - 2 * (1 - h)), lane);
+                dl[s] = frag(sw.D[1 - h], 2 * (s - 2 * (1 - h)) + 1, lane);
             }
-
-            bf16x8 uh[4], ul[4];
-            if (WITH_O) {
+            if (WITH_O && h == 1) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    if (s < 2 * h + 2) acc_to_b_split(U[s >> 1], s, uh[s], ul[s]);
+                for (int s = 0; s < 2; ++s) {
+                    uh[s] = frag(sw.Uo, 2 * s, lane);
+                    ul[s] = frag(sw.Uo, 2 * s + 1, lane);
+                }
+            }
+            if (WITH_O) {
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) {
                     const f32x4 e = *reinterpret_cast<const f32x4*>(&S.tab[1][32 * h + 8 * j4 + 4 * h2]);
@@ -301,14 +324,6 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                 }
             }
             // S <- e^{gamma_n} S + U'^T diag(e^{gamma_n - gamma}) K (this wave's tiles) and O = Y + P U'
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const f32x4 d = *reinterpret_cast<const f32x4*>(&S.tab[2][32 * rt + 8 * j4 + 4 * h2]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) U[rt][4 * j4 + i] *= d[i];
-                }
             const float decay = S.tab[3][CH - 1];
 #pragma unroll
             for (int i = 0; i < HT; ++i)
@@ -316,13 +331,11 @@ gdn_scan_split_kernel(const int32_t* __restrict__ cu, int B, int Hv,
                 for (int j = 0; j < 16; ++j) St[i][j] *= decay;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                bf16x8 dh, dl;
-                acc_to_b_split(U[s >> 1], s, dh, dl);
 #pragma unroll
                 for (int i = 0; i < HT; ++i) {
                     const bf16x8 a = frag(S.KT, s * KT_TILES + h * HT + i, lane);
-                    St[i] = mma32(a, dh, St[i]);
-                    St[i] = mma32(a, dl, St[i]);
+                    St[i] = mma32(a, dh[s], St[i]);
+                    St[i] = mma32(a, dl[s], St[i]);
                 }
                 if (WITH_O && s < 2 * h + 2) {                 // P is lower triangular
                     const int f = h == 0 ? s : 2 + s;
