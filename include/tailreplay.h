@@ -195,10 +195,12 @@ tr_schedule tr_gdn_get_schedule(void);
  *   stream        hipStream_t to enqueue on
  * Arithmetic is fp32 token by token for both input types (bf16 keys are converted
  * exactly): a long product of operators keeps every rounding it meets, so the chunked bf16
- * path is not used here.  The product is associative, so with few (sequence, head) pairs
- * each span is cut into segments that run side by side from I, and each head's segment
- * products are then multiplied in order (fp32); the cut depends only on the lengths, Hv and
- * d.  An empty sequence gives phi_out = I (and log scale 0).
+ * path is not used here.  The decays are scalars and are kept out of the matrix product;
+ * with log_scale_out NULL, exp(sum g) is applied once at the end.  The product is
+ * associative, so with few (sequence, head) pairs each span is cut into segments that run
+ * side by side from I, and each head's segment products are then multiplied in order (fp32
+ * MFMA); the cut depends only on the lengths, Hv and d.  An empty sequence gives phi_out = I
+ * (and log scale 0).
  * Errors: as for tr_gdn_replay (TR_ERR_WORKSPACE for a missing or short workspace).
  * ------------------------------------------------------------------------------- */
 tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,

@@ -310,8 +310,10 @@ hipError_t launch_gdn(const tr::GdnArgs& a, tr_dtype dt, hipStream_t s) {
 // Segments of tr_gdn_transition.  The product of a span's operators is associative, so with
 // few (sequence, head) pairs to run, each span is cut into segments of seg_len tokens that run
 // side by side from I, and their products are multiplied in order afterwards.  The plan aims
-// the segments at kTransitionWgs workgroups of 16 rows (three per CU on 256 CUs) and depends
-// only on the lengths, the head count and d, so a result does not change with the device.
+// the segments at kTransitionWgs workgroups of 16 rows (three per CU on 256 CUs; four, as many
+// as their LDS allows, cost one more product in the chain and measured no faster on a
+// 1,639-token span of 16 heads) and depends only on the lengths, the head count and d, so a
+// result does not change with the device.
 constexpr int64_t kTransitionWgs = 768;
 constexpr int64_t kTransitionMinSeg = 128;   // shorter segments cost more to multiply than to run
 constexpr int64_t kTransitionMaxSegs = 16;   // the products are multiplied one after another
@@ -321,7 +323,7 @@ struct TransitionPlan {
 };
 TransitionPlan transition_plan(const int32_t* cu, int32_t B, int32_t Hv, int32_t d, int32_t max_len) {
     TransitionPlan p;
-    const int64_t per_seq = (int64_t)Hv * (d / 16);    // workgroups of one sequence's whole span
+    const int64_t per_seq = (int64_t)Hv * (d / tr::kTransitionRows);   // workgroups of one whole span
     if ((int64_t)B * per_seq * 2 > kTransitionWgs) return p;
     const int64_t segs = (kTransitionWgs + per_seq - 1) / per_seq;   // segments in all
     int64_t seg = std::max<int64_t>(((int64_t)cu[B] + segs - 1) / segs, kTransitionMinSeg);
@@ -534,8 +536,7 @@ tr_status tr_gdn_transition(const void* k, const float* g, const float* beta,
     a.log_scale_out = log_scale_out;
     a.uniform_len = 0; a.state_bstride = (int64_t)Hv * d * d;
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = (dt == TR_BF16) ? tr::launch_gdn_token_f32_bf16in(a, s, plan.sg)
-                                         : tr::launch_gdn_token_f32(a, s, plan.sg);
+    const hipError_t e = tr::launch_gdn_transition(a, dt == TR_BF16, plan.sg, s);
     return finish_launch(e, s, fn);
 }
 

@@ -1,5 +1,4 @@
-// Token-serial Gated DeltaNet recurrence in fp32, for fp32 inputs and for the transition
-// product of any inputs.
+// Token-serial Gated DeltaNet recurrence in fp32, for fp32 inputs.
 //
 // Reading notes "Tail-Replay：混合 LLM 前缀缓存的短尾重放机制", section 2.3, Eq. (1), with
 // the state stored dv x dk: S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,
@@ -15,12 +14,7 @@
 // thread.  Keys (and queries, with outputs) of 64 tokens are staged in LDS, double-buffered:
 // the next chunk's loads are issued into registers before the current chunk is processed, and
 // written to the other buffer after it.  This path serves fp32 inputs, where bf16 MFMA
-// operands would not be exact, and the transition product of bf16 inputs, which wants fp32
-// arithmetic (its inputs are read as bf16 and converted exactly).
-//
-// The transition product T_1 ... T_n is associative, so a long span with few heads is cut into
-// segments that run side by side, each from I (segment mode, seg_len > 0), and
-// transition_chain_kernel multiplies each head's segment products in order.
+// operands would not be exact.
 #include "internal.h"
 
 namespace tr {
@@ -55,8 +49,7 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                      const TI* __restrict__ v, const float* __restrict__ g,
                      const float* __restrict__ beta, const int32_t* __restrict__ cu,
                      int Hqk, int Hv, int DV, float q_scale, int uniform_len, long long state_bstride,
-                     const float* state_in, int state_identity, float* state_out, TI* __restrict__ o,
-                     float* log_scale_out, int seg_len, int seg_max, float* seg_phi, float* seg_log)
+                     const float* state_in, float* state_out, TI* __restrict__ o)
 {
     constexpr int E = DK / LPR;                         // key columns per lane
     constexpr int VEC = 16 / sizeof(TI);                // inputs per 16-byte load
@@ -64,42 +57,25 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
     static_assert(KLOADS * VEC * NTH == TC * DK, "staging covers the chunk");
     __shared__ __align__(16) TI sK[2][TC][DK];
     __shared__ __align__(16) TI sQ[WITH_O ? 2 : 1][WITH_O ? TC : 1][DK];
-    __shared__ float sA[2][TC], sB[2][TC], sG[2][TC];
+    __shared__ float sA[2][TC], sB[2][TC];
     __shared__ float sV[2][TC][ROWS];
 
     const int row_blocks = DV / ROWS;
-    const int item = (int)blockIdx.x;
+    const int item = (int)blockIdx.x;                   // (sequence, head, row block)
     const int hv = (item / row_blocks) % Hv;
     const int rb = item % row_blocks;
-    // segment mode: items are (sequence, segment, head, row block); otherwise (sequence, head, row block)
-    const int bs = item / (Hv * row_blocks);
-    const int b = seg_len > 0 ? bs / seg_max : bs;
-    const int seg = seg_len > 0 ? bs % seg_max : 0;
+    const int b = item / (Hv * row_blocks);
     const int hq = hv / (Hv / Hqk);
     const int tid = (int)threadIdx.x;
     const int lr = tid / LPR, j = tid % LPR;
     const int r = rb * ROWS + lr;                       // state row (value index)
-    int bos = cu ? cu[b] : b * uniform_len;
-    int len = cu ? cu[b + 1] - bos : uniform_len;
-    // a sequence of one segment (or none) writes its result in place; longer ones write each
-    // segment's product to the records for transition_chain_kernel
-    bool to_records = false;
-    if (seg_len > 0) {
-        const int nseg = max(1, (len + seg_len - 1) / seg_len);
-        if (seg >= nseg) return;                        // the whole workgroup, before any barrier
-        to_records = nseg > 1;
-        bos += seg * seg_len;
-        len = min(seg_len, len - seg * seg_len);
-    }
-    const size_t sbase = to_records
-        ? (((size_t)bs * Hv + hv) * DV + r) * DK + (size_t)j * E
-        : (size_t)b * state_bstride + ((size_t)hv * DV + r) * DK + (size_t)j * E;
-    float* const out = to_records ? seg_phi : state_out;
+    const int bos = cu ? cu[b] : b * uniform_len;
+    const int len = cu ? cu[b + 1] - bos : uniform_len;
+    const size_t sbase = (size_t)b * state_bstride + ((size_t)hv * DV + r) * DK + (size_t)j * E;
 
     float S[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        S[e] = state_identity ? (j * E + e == r ? 1.f : 0.f) : (state_in ? state_in[sbase + e] : 0.f);
+    for (int e = 0; e < E; ++e) S[e] = state_in ? state_in[sbase + e] : 0.f;
 
     // chunk staging registers: keys (and queries), this workgroup's values, gates
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -126,7 +102,6 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
             rbeta = tid < n ? beta[(size_t)(bos + c0 + tid) * Hv + hv] : 0.f;
         }
     };
-    float log_sum = 0.f;                                // thread 0: sum of g over the span
     auto put = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < KLOADS; ++i) {
@@ -141,10 +116,8 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
             sV[buf][idx / ROWS][idx % ROWS] = rv[i];
         }
         if (tid < TC) {
-            // with log_scale_out, the decay is kept out of S and its log summed instead
-            sA[buf][tid] = log_scale_out ? 1.f : __expf(ra);
+            sA[buf][tid] = __expf(ra);
             sB[buf][tid] = rbeta;
-            sG[buf][tid] = ra;
         }
     };
 
@@ -158,8 +131,6 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         const int n = min(TC, len - c0);
         const bool more = c0 + TC < len;
         if (more) fetch(c0 + TC);                       // lands while this chunk is processed
-        if (log_scale_out && tid == 0)
-            for (int t = 0; t < n; ++t) log_sum += sG[buf][t];     // in token order
         for (int t = 0; t < n; ++t) {
             float kv[E];
             load_f32<E>(&sK[buf][t][j * E], kv);
@@ -195,129 +166,36 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) out[sbase + e] = S[e];
-    if (log_scale_out && tid == 0 && rb == 0) {
-        if (to_records) seg_log[(size_t)bs * Hv + hv] = log_sum;
-        else log_scale_out[(size_t)b * Hv + hv] = log_sum;
-    }
-}
-
-// Phi = P_0 P_1 ... P_{nseg-1} for every (sequence, head) cut into several segments, from the
-// segment products P_s (and log scale = the sum of the segments' log scales, in order).  A
-// workgroup of 256 threads takes 16 rows of one head's Phi with the lane layout of the token
-// kernel: the row block of P_0 times each later P_s in turn, every P_s staged through LDS 64
-// rows at a time.  fp32 throughout; the factors have norm at most 1 for beta |k|^2 <= 2.
-template <int DK>
-__global__ void __launch_bounds__(NTH)
-transition_chain_kernel(const int32_t* __restrict__ cu, int Hv, int seg_len, int seg_max,
-                        const float* __restrict__ seg_phi, const float* __restrict__ seg_log,
-                        float* __restrict__ phi_out, float* __restrict__ log_scale_out)
-{
-    constexpr int E = DK / LPR;
-    constexpr int HR = 64;                              // rows of P_s per staging step
-    __shared__ __align__(16) float sR[ROWS][DK];
-    __shared__ __align__(16) float sP[HR][DK];
-    const int row_blocks = DK / ROWS;
-    const int item = (int)blockIdx.x;
-    const int b = item / (Hv * row_blocks);
-    const int hv = (item / row_blocks) % Hv;
-    const int rb = item % row_blocks;
-    const int len = cu[b + 1] - cu[b];
-    const int nseg = max(1, (len + seg_len - 1) / seg_len);
-    if (nseg < 2) return;                               // written in place by the segment pass
-    const int tid = (int)threadIdx.x;
-    const int lr = tid / LPR, j = tid % LPR;
-    const size_t mat = (size_t)DK * DK;
-    auto factor = [&](int s) { return seg_phi + ((size_t)(b * seg_max + s) * Hv + hv) * mat; };
-    const size_t roff = (size_t)(rb * ROWS + lr) * DK + (size_t)j * E;
-    float R[E];
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(factor(0) + roff + e);
-        R[e] = x[0]; R[e + 1] = x[1]; R[e + 2] = x[2]; R[e + 3] = x[3];
-    }
-    for (int s = 1; s < nseg; ++s) {
-        const float* P = factor(s);
-        __syncthreads();                                // every thread is done with sR and sP
-#pragma unroll
-        for (int e = 0; e < E; e += 4) *reinterpret_cast<f32x4*>(&sR[lr][j * E + e]) = f32x4{R[e], R[e + 1], R[e + 2], R[e + 3]};
-        float acc[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = 0.f;
-        for (int h = 0; h < DK; h += HR) {
-            if (h > 0) __syncthreads();                 // every thread is done with the last rows
-#pragma unroll
-            for (int i = 0; i < HR * DK / 4 / NTH; ++i) {
-                const int idx = (tid + NTH * i) * 4;
-                *reinterpret_cast<f32x4*>(&sP[idx / DK][idx % DK]) =
-                    *reinterpret_cast<const f32x4*>(P + (size_t)(h + idx / DK) * DK + idx % DK);
-            }
-            __syncthreads();
-#pragma unroll 4
-            for (int i = 0; i < HR; ++i) {
-                const float x = sR[lr][h + i];
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = fmaf(x, sP[i][j * E + e], acc[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) R[e] = acc[e];
-    }
-#pragma unroll
-    for (int e = 0; e < E; e += 4)
-        *reinterpret_cast<f32x4*>(phi_out + ((size_t)b * Hv + hv) * mat + roff + e) = f32x4{R[e], R[e + 1], R[e + 2], R[e + 3]};
-    if (log_scale_out && rb == 0 && tid == 0) {
-        float ls = 0.f;
-        for (int s = 0; s < nseg; ++s) ls += seg_log[(size_t)(b * seg_max + s) * Hv + hv];
-        log_scale_out[(size_t)b * Hv + hv] = ls;
-    }
+    for (int e = 0; e < E; ++e) state_out[sbase + e] = S[e];
 }
 
 template <int DK, typename TI>
-hipError_t launch_dk(const GdnArgs& a, const Segments& sg, hipStream_t stream) {
-    const unsigned sets = (unsigned)(sg.seg_len > 0 ? a.B * sg.seg_max : a.B);
-    const dim3 grid(sets * (unsigned)(a.Hv * (a.dv / ROWS)));
+hipError_t launch_dk(const GdnArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.B * a.Hv * (a.dv / ROWS)));
     if (a.o) {
         hipLaunchKernelGGL((gdn_token_f32_kernel<DK, TI, true>), grid, dim3(NTH), 0, stream,
                            (const TI*)a.q, (const TI*)a.k, (const TI*)a.v, a.g, a.beta,
                            a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
-                           a.state_in, a.state_identity, a.state_out, (TI*)a.o, a.log_scale_out,
-                           sg.seg_len, sg.seg_max, sg.phi, sg.log);
+                           a.state_in, a.state_out, (TI*)a.o);
     } else {
         hipLaunchKernelGGL((gdn_token_f32_kernel<DK, TI, false>), grid, dim3(NTH), 0, stream,
                            (const TI*)a.q, (const TI*)a.k, (const TI*)a.v, a.g, a.beta,
                            a.cu_seqlens, a.Hqk, a.Hv, a.dv, a.q_scale, a.uniform_len, (long long)a.state_bstride,
-                           a.state_in, a.state_identity, a.state_out, (TI*)nullptr, a.log_scale_out,
-                           sg.seg_len, sg.seg_max, sg.phi, sg.log);
+                           a.state_in, a.state_out, (TI*)nullptr);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || sg.seg_len <= 0) return e;
-    const dim3 cgrid((unsigned)(a.B * a.Hv * (DK / ROWS)));
-    hipLaunchKernelGGL((transition_chain_kernel<DK>), cgrid, dim3(NTH), 0, stream, a.cu_seqlens, a.Hv,
-                       sg.seg_len, sg.seg_max, (const float*)sg.phi, (const float*)sg.log, a.state_out,
-                       a.log_scale_out);
     return hipGetLastError();
 }
 
 template <typename TI>
-hipError_t launch_token(const GdnArgs& a, const Segments& sg, hipStream_t stream) {
-    if (a.dv % ROWS != 0) return hipErrorInvalidValue;
-    // segments start from I and need the packed lengths on the device
-    if (sg.seg_len > 0 && (!a.state_identity || a.o || a.v || a.state_in || !a.cu_seqlens || a.dk != a.dv ||
-                           sg.seg_max < 2 || !sg.phi || (a.log_scale_out && !sg.log)))
-        return hipErrorInvalidValue;
-    if (a.dk == 128) return launch_dk<128, TI>(a, sg, stream);
-    if (a.dk == 64) return launch_dk<64, TI>(a, sg, stream);
+hipError_t launch_token(const GdnArgs& a, hipStream_t stream) {
+    if (a.dv % ROWS != 0 || a.state_identity || a.log_scale_out) return hipErrorInvalidValue;
+    if (a.dk == 128) return launch_dk<128, TI>(a, stream);
+    if (a.dk == 64) return launch_dk<64, TI>(a, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream, const Segments& sg) {
-    return launch_token<float>(a, sg, stream);
-}
-hipError_t launch_gdn_token_f32_bf16in(const GdnArgs& a, hipStream_t stream, const Segments& sg) {
-    return launch_token<__bf16>(a, sg, stream);
-}
+hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream) { return launch_token<float>(a, stream); }
 
 }  // namespace tr

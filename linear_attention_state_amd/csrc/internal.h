@@ -49,8 +49,8 @@ struct GdnArgs {
     float q_scale;
     const float* state_in;       // may be null (zero state)
     int32_t state_identity;      // 1: start every (sequence, head) from I (dk == dv); state_in unused
-    float* log_scale_out;        // non-null (fp32 token path only): run with alpha = 1 and write
-                                 // sum(g) per (sequence, head) here, [B, Hv]
+    float* log_scale_out;        // transition only: non-null keeps the decay out of state_out
+                                 // and writes sum(g) per (sequence, head) here, [B, Hv]
     float* state_out;
     void* o;                     // may be null (state-only)
     int32_t max_len;             // longest sequence (host-computed)
@@ -96,21 +96,23 @@ struct SplitPlan {
 };
 hipError_t launch_gdn_prep_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
 hipError_t launch_gdn_scan_split_bf16(const GdnArgs& a, const SplitPlan& plan, hipStream_t stream);
-// Segments of the transition product (state_identity, no values, no outputs): with seg_len > 0
-// every sequence of n tokens is cut into max(1, ceil(n / seg_len)) <= seg_max segments that run
-// side by side, each from I; a sequence of several segments writes their products to
-// phi[(b * seg_max + s) * Hv + h] ([dk, dk] each) and log scales to log[(b * seg_max + s) * Hv + h],
-// and a second kernel multiplies them in order into state_out / log_scale_out.
+// Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
+hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream);
+
+// Transition product of a span from I with no values (gdn_transition.hip); a.state_out receives
+// [B, Hv, d, d] and a.log_scale_out (if non-null) the gate sums, else the decay is applied.
+// With seg_len > 0 every sequence of n tokens is cut into max(1, ceil(n / seg_len)) <= seg_max
+// segments that run side by side, each from I; a sequence of several segments writes their
+// products to phi[(b * seg_max + s) * Hv + h] ([d, d] each) and gate sums to
+// log[(b * seg_max + s) * Hv + h], and a second kernel multiplies them in order.
+constexpr int kTransitionRows = 16;   // rows of one head's product per segment workgroup
 struct Segments {
     int32_t seg_len = 0;     // 0: one pass over every whole sequence
     int32_t seg_max = 1;
     float* phi = nullptr;
     float* log = nullptr;
 };
-// Token-serial recurrence in fp32 for fp32 inputs (gdn_token_f32.hip).
-hipError_t launch_gdn_token_f32(const GdnArgs& a, hipStream_t stream, const Segments& sg = Segments());
-// The same fp32 arithmetic on bf16 inputs (and bf16 outputs).
-hipError_t launch_gdn_token_f32_bf16in(const GdnArgs& a, hipStream_t stream, const Segments& sg = Segments());
+hipError_t launch_gdn_transition(const GdnArgs& a, bool keys_bf16, const Segments& sg, hipStream_t stream);
 
 // State algebra and single-token steps (state_ops.hip).
 // out[n] = exp(log_scale[n]) S_c[n] Phi[n] (+ S_hat[n]) for n < N (log_scale may be null); S_c, S_hat, out [N, dv, dk], Phi [N, dk, dk], fp32.

@@ -53,7 +53,7 @@ PHI_TOL = 1e-5
 
 
 @pytest.mark.parametrize("d,dtype,tol", [(128, torch.bfloat16, PHI_TOL), (64, torch.bfloat16, PHI_TOL),
-                                         (64, torch.float32, 1e-5)])
+                                         (128, torch.float32, PHI_TOL), (64, torch.float32, PHI_TOL)])
 def test_transition_matches_oracle(d, dtype, tol):
     lens = [130, 64, 1, 0, 77]
     inp = synthetic.gdn_inputs(lens, 2, 4, d, d, dtype=dtype, seed=11)
