@@ -78,11 +78,11 @@ __device__ __forceinline__ bf16x8 kperm(const bf16* row, int s, int h) {
 }
 __device__ __forceinline__ void acc_to_b_split(const f32x16& t, int s, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float x = t[8 * (s & 1) + i];
-        const bf16 xh = (bf16)x;
-        hi[i] = xh;
-        lo[i] = (bf16)(x - (float)xh);
+    for (int i = 0; i < 8; i += 2) {
+        bf16x2 h, l;
+        split2(t[8 * (s & 1) + i], t[8 * (s & 1) + i + 1], h, l);
+        hi[i] = h[0]; hi[i + 1] = h[1];
+        lo[i] = l[0]; lo[i + 1] = l[1];
     }
 }
 __device__ __forceinline__ bf16x8 acc_to_b(const f32x16& t, int s) {
@@ -643,13 +643,12 @@ gdn_chunk_bf16_kernel(const SeqOrder order, int ordered, const bf16* __restrict_
                         const int c0 = 16 * cb + 4 * g4;
                         const float gt = sm.g2[t];
                         const f32x4 gi = tab4(sm.g2, c0);
-                        bf16x4 ph, pl;
+                        f32x4 p;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float p = (c0 + j <= t) ? q_scale * __builtin_amdgcn_exp2f(gt - gi[j]) * tacc[it][j] : 0.f;
-                            ph[j] = (bf16)p;
-                            pl[j] = (bf16)(p - (float)ph[j]);
-                        }
+                        for (int j = 0; j < 4; ++j)
+                            p[j] = (c0 + j <= t) ? q_scale * __builtin_amdgcn_exp2f(gt - gi[j]) * tacc[it][j] : 0.f;
+                        bf16x4 ph, pl;
+                        split_bf4(p, ph, pl);
                         *reinterpret_cast<bf16x4*>(&sm.np.p.Ph[t][c0]) = ph;
                         *reinterpret_cast<bf16x4*>(&sm.np.p.Pl[t][c0]) = pl;
                     }

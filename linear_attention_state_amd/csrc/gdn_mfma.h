@@ -37,11 +37,26 @@ __device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f
 // A and B operand layouts of that instruction are the row and accumulator layouts):
 // X Y ~ Xhi Yhi + Xhi Ylo + Xlo Yhi, leaving out Xlo Ylo (about 2^-16 of |X| |Y| per term),
 // small terms first.  Three 16x16x16 products instead of four fp32 16x16x4 ones.
+// x ~ hi + lo for two values: hi = bf16(x), lo = bf16(x - hi).  x - hi is exact in fp32 (the
+// rounding error of a rounding to fewer bits), so v_dot2_f32_bf16 of the packed hi pair with
+// (-1, -0) or (-0, -1), accumulated onto x, forms it in one instruction instead of widening
+// hi back to fp32 and subtracting; the result is the same bits.  The zero of each selector is
+// -0 so that neither pair matches an inline constant: the compiler encodes (-1, +0) as the
+// inline constant -1.0, which the hardware does not read as that bf16 pair (measured: every
+// lane wrong), while literal selectors give x - hi exactly.
+__device__ __forceinline__ void split2(float x0, float x1, bf16x2& hi, bf16x2& lo) {
+    hi = bf16x2{(bf16)x0, (bf16)x1};
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hi, bf16x2{(bf16)-1.f, (bf16)-0.f}, x0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hi, bf16x2{(bf16)-0.f, (bf16)-1.f}, x1, false);
+    lo = bf16x2{(bf16)r0, (bf16)r1};
+}
 __device__ __forceinline__ void split_bf4(const f32x4& x, bf16x4& hi, bf16x4& lo) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (bf16)x[i];
-        lo[i] = (bf16)(x[i] - (float)hi[i]);
+    for (int i = 0; i < 4; i += 2) {
+        bf16x2 h, l;
+        split2(x[i], x[i + 1], h, l);
+        hi[i] = h[0]; hi[i + 1] = h[1];
+        lo[i] = l[0]; lo[i + 1] = l[1];
     }
 }
 __device__ __forceinline__ f32x4 mm16x3(const f32x4& xrow, const f32x4& yacc, f32x4 c) {

@@ -26,7 +26,7 @@
 // before the loop turns.  Every LDS read is one lane's 16 bytes of a fragment (conflict-free, and a
 // plain read: the compiler can then tell that the next stage's loads do not touch the
 // stage being read, and adds no wait for them).
-#include "internal.h"
+#include "gdn_mfma.h"
 
 #include <type_traits>
 
@@ -69,11 +69,11 @@ __device__ __forceinline__ bf16x8 acc_to_b(const f32x16& t, int s) {
 }
 __device__ __forceinline__ void acc_to_b_split(const f32x16& t, int s, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float x = t[8 * (s & 1) + i];
-        const bf16 xh = (bf16)x;
-        hi[i] = xh;
-        lo[i] = (bf16)(x - (float)xh);
+    for (int i = 0; i < 8; i += 2) {
+        bf16x2 h, l;
+        gdn::split2(t[8 * (s & 1) + i], t[8 * (s & 1) + i + 1], h, l);
+        hi[i] = h[0]; hi[i + 1] = h[1];
+        lo[i] = l[0]; lo[i + 1] = l[1];
     }
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
