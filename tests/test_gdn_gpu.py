@@ -102,6 +102,28 @@ def test_bf16_ragged_given_state_and_scale(dk, dv, schedule):
     run_and_compare(inp, state_in=s_in, q_scale=dk ** -0.5, label="bf16 state_in %dx%d %s" % (dk, dv, schedule))
 
 
+def test_bf16_ragged_unit_write_strength(schedule):
+    # beta = 1 on every token (the write fully replaces the value along k_t); gates as in the
+    # workloads.  beta = 0 is test_beta_zero_is_pure_decay_on_gpu; beta = 2 (a reflector per
+    # token) is held to the fp32 path's bound in test_fp32_ragged_reflectors, since the bf16
+    # plan's states land just above 2e-3 there (about 2.2e-3 in tests/precision_model.py at
+    # 130 to 1,639 tokens).
+    inp = synthetic.gdn_inputs(RAGGED, 2, 4, 128, 128, seed=411)
+    inp.beta = torch.ones_like(inp.beta)
+    run_and_compare(inp, label="bf16 beta = 1 %s" % schedule)
+
+
+def test_fp32_ragged_reflectors():
+    # beta = 2, alpha = 1: every step applies the Householder reflector I - 2 k k^T (unit keys)
+    # to the state, and nothing decays
+    inp = synthetic.gdn_inputs(RAGGED, 2, 4, 128, 128, dtype=torch.float32, seed=412)
+    inp.beta = torch.full_like(inp.beta, 2.0)
+    inp.g = torch.zeros_like(inp.g)
+    rng = np.random.default_rng(13)
+    s_in = (rng.standard_normal((len(RAGGED), 4, 128, 128)) * 0.3).astype(np.float32)
+    run_and_compare(inp, state_in=s_in, stol=F32_TOL, otol=F32_TOL, label="fp32 reflectors")
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
 def test_fp32_ragged(dk, dv):
     inp = synthetic.gdn_inputs(RAGGED, 2, 4, dk, dv, dtype=torch.float32, seed=3 + dk)

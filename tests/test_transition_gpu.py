@@ -99,6 +99,30 @@ def test_transition_in_segments(lens, Hv, min_segments):
         assert np.array_equal(np64(psi[lens.index(0), 0]), np.eye(d))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_transition_of_reflectors(dtype):
+    # alpha = 1 and beta = 2 make every factor I - 2 k k^T a Householder reflector (for unit
+    # keys): nothing decays, so every rounding stays in the product.  2,000 tokens on two heads
+    # are cut into 16 segments and multiplied back, and Phi must still match the oracle.
+    d, lens, H = 128, [2000], 2
+    inp = synthetic.gdn_inputs(lens, H, H, d, d, dtype=dtype, seed=23)
+    g = torch.zeros_like(inp.g)
+    beta = torch.full_like(inp.beta, 2.0)
+    n_ws = gdn_transition_workspace_size(inp.cu_seqlens, H, H, d, dtype)
+    assert n_ws >= 16 * H * d * d * 4
+    phi = gdn_transition(inp.k.cuda(), g.cuda(), beta.cuda(), inp.cu_seqlens)
+    torch.cuda.synchronize()
+    ref = oracle_phi(np64(inp.k), np64(g), np64(beta), inp.cu_seqlens.numpy(), d)
+    worst = max(rel(np64(phi[0, h]), ref[0, h]) for h in range(H))
+    print("reflectors %s: worst err %.3e" % (dtype, worst), flush=True)
+    assert worst <= PHI_TOL
+    if dtype == torch.float32:
+        # unit keys to fp32 rounding: the product stays orthogonal to about the same accuracy
+        for h in range(H):
+            P = np64(phi[0, h])
+            assert np.linalg.norm(P.T @ P - np.eye(d)) / np.sqrt(d) <= 1e-4
+
+
 def test_compose_matches_definition():
     gen = torch.Generator(device="cpu").manual_seed(3)
     S_c = torch.randn((6, 128, 128), generator=gen)
