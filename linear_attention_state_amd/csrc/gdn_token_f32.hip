@@ -7,14 +7,17 @@
 // evolves on its own: row r needs only its own dot product with k_t and entry r of v_t.
 //
 // Work decomposition: a workgroup of 256 threads takes 16 rows of one (sequence, value head);
-// a row is spread over 16 lanes, lane j holding key columns [j E, j E + E), E = dk / 16.  Per
+// a row is spread over 16 lanes, lane j holding E = dk / 16 key columns in groups of four,
+// 4 j + 64 g + {0..3} for group g, so that the 16 lanes' 16-byte LDS reads of a key (or query)
+// row are contiguous and free of bank conflicts.  Per
 // token a row costs E fused multiply-adds per lane for S k, a four-step sum across its 16
 // lanes (DPP row rotations, so every lane ends with the total), and E more for the update:
 // the serial chain per token is a few dozen cycles instead of dk dependent steps in one
 // thread.  Keys (and queries, with outputs) of 64 tokens are staged in LDS, double-buffered:
 // the next chunk's loads are issued into registers before the current chunk is processed, and
-// written to the other buffer after it.  This path serves fp32 inputs, where bf16 MFMA
-// operands would not be exact.
+// written to the other buffer after it; tokens go four at a time, so the LDS reads of the
+// next tokens are issued ahead of the current token's dependent chain.  This path serves fp32
+// inputs, where bf16 MFMA operands would not be exact.
 #include "internal.h"
 
 namespace tr {
@@ -71,11 +74,12 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
     const int r = rb * ROWS + lr;                       // state row (value index)
     const int bos = cu ? cu[b] : b * uniform_len;
     const int len = cu ? cu[b + 1] - bos : uniform_len;
-    const size_t sbase = (size_t)b * state_bstride + ((size_t)hv * DV + r) * DK + (size_t)j * E;
+    const size_t sbase = (size_t)b * state_bstride + ((size_t)hv * DV + r) * DK;
+    auto col = [&](int e) { return 4 * LPR * (e / 4) + 4 * j + e % 4; };   // key column of S[e]
 
     float S[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) S[e] = state_in ? state_in[sbase + e] : 0.f;
+    for (int e = 0; e < E; ++e) S[e] = state_in ? state_in[sbase + col(e)] : 0.f;
 
     // chunk staging registers: keys (and queries), this workgroup's values, gates
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -131,9 +135,10 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         const int n = min(TC, len - c0);
         const bool more = c0 + TC < len;
         if (more) fetch(c0 + TC);                       // lands while this chunk is processed
-        for (int t = 0; t < n; ++t) {
+        auto step = [&](int t) {
             float kv[E];
-            load_f32<E>(&sK[buf][t][j * E], kv);
+#pragma unroll
+            for (int e = 0; e < E; e += 4) load_f32<4>(&sK[buf][t][col(e)], kv + e);
             const float a = sA[buf][t], bt = sB[buf][t], vr = sV[buf][t][lr];
             float p0 = 0.f, p1 = 0.f;
 #pragma unroll
@@ -147,7 +152,8 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
             for (int e = 0; e < E; ++e) S[e] = fmaf(a, S[e], coef * kv[e]);
             if (WITH_O) {
                 float qv[E];
-                load_f32<E>(&sQ[WITH_O ? buf : 0][WITH_O ? t : 0][j * E], qv);
+#pragma unroll
+                for (int e = 0; e < E; e += 4) load_f32<4>(&sQ[WITH_O ? buf : 0][WITH_O ? t : 0][col(e)], qv + e);
                 float s0 = 0.f, s1 = 0.f;
 #pragma unroll
                 for (int e = 0; e < E; e += 2) {
@@ -157,7 +163,13 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
                 const float so = row16_sum(s0 + s1);
                 if (j == 0) o[((size_t)(bos + c0 + t) * Hv + hv) * DV + r] = (TI)(q_scale * so);
             }
+        };
+        int t = 0;
+        for (; t + 4 <= n; t += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) step(t + u);
         }
+        for (; t < n; ++t) step(t);
         __syncthreads();                                // every thread is done with buffer buf
         if (more) {
             put(buf ^ 1);
@@ -166,7 +178,7 @@ gdn_token_f32_kernel(const TI* __restrict__ q, const TI* __restrict__ k,
         }
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) state_out[sbase + e] = S[e];
+    for (int e = 0; e < E; ++e) state_out[sbase + col(e)] = S[e];
 }
 
 template <int DK, typename TI>
