@@ -46,17 +46,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Workgroups are dealt to the 8 XCDs round robin by index.  Item -> (pair, row block) such that
-// the rb_count row blocks of one pair share an XCD and so its L2: the keys (or the factors)
-// they all read are then fetched from memory once per pair.  A grid of
-// 8 rb_count ceil(pairs / 8) items covers every pair; items past the last pair have nothing to do.
-__device__ __forceinline__ void xcd_item(int item, int rb_count, int& pair, int& rb) {
-    const int xcd = item % 8, slot = item / 8;
-    pair = (slot / rb_count) * 8 + xcd;
-    rb = slot % rb_count;
-}
-inline unsigned xcd_grid(long long pairs, int rb_count) { return (unsigned)(8 * rb_count * ((pairs + 7) / 8)); }
-
 // 16 bytes of inputs as fp32 (bf16 converts exactly).
 template <typename TI>
 __device__ __forceinline__ void to_f32(const u32x4& w, float* out) {
@@ -304,14 +293,14 @@ template <int D, typename TI>
 hipError_t launch_d(const GdnArgs& a, const Segments& sg, hipStream_t stream) {
     const long long sets = sg.seg_len > 0 ? (long long)a.B * sg.seg_max : (long long)a.B;
     const long long pairs = sets * a.Hv;
-    if (8 * (D / 16) * ((pairs + 7) / 8) > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((transition_segment_kernel<D, TI>), dim3(xcd_grid(pairs, D / ROWS)), dim3(NTH), 0, stream,
+    if (xcd_grid(pairs, D / ROWS) > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((transition_segment_kernel<D, TI>), dim3((unsigned)xcd_grid(pairs, D / ROWS)), dim3(NTH), 0, stream,
                        (const TI*)a.k, a.g, a.beta, a.cu_seqlens, a.Hqk, a.Hv, sg.seg_len, sg.seg_max, (int)pairs,
                        sg.phi, sg.log, a.state_out, a.log_scale_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sg.seg_len <= 0) return e;
     const long long heads = (long long)a.B * a.Hv;
-    hipLaunchKernelGGL((transition_chain_kernel<D>), dim3(xcd_grid(heads, D / 16)), dim3(D * 4), 0, stream,
+    hipLaunchKernelGGL((transition_chain_kernel<D>), dim3((unsigned)xcd_grid(heads, D / 16)), dim3(D * 4), 0, stream,
                        a.cu_seqlens, a.Hv, sg.seg_len, sg.seg_max, (int)heads, (const float*)sg.phi,
                        (const float*)sg.log, a.state_out, a.log_scale_out);
     return hipGetLastError();

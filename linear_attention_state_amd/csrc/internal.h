@@ -35,6 +35,18 @@ inline int device_cu_count() {
     return n;
 }
 
+// Workgroups are dealt to the 8 XCDs round robin by index.  Item -> (pair, row block) such
+// that the rb_count row blocks of one pair (a matrix, or a (sequence, head)) share an XCD and so
+// its L2: the operands they all read are then fetched from memory once per pair.  A grid of
+// xcd_grid(pairs, rb_count) = 8 rb_count ceil(pairs / 8) items covers every pair; items past
+// the last pair have nothing to do.
+__device__ __forceinline__ void xcd_item(int item, int rb_count, int& pair, int& rb) {
+    const int xcd = item % 8, slot = item / 8;
+    pair = (slot / rb_count) * 8 + xcd;
+    rb = slot % rb_count;
+}
+inline long long xcd_grid(long long pairs, int rb_count) { return 8LL * rb_count * ((pairs + 7) / 8); }
+
 // One tr_gdn_replay request after host-side validation.
 struct GdnArgs {
     const void* q;

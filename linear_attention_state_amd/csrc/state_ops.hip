@@ -16,50 +16,57 @@ typedef __bf16 bf16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- out = e^ls S_c Phi (+ S_hat)
-// One 64x64 output tile per workgroup of 256 threads (4x4 outputs each), k in slices of 32
-// through LDS.  fp32 throughout.
-__global__ void __launch_bounds__(256)
+// fp32 MFMA (16x16x4).  A workgroup of DK / 16 waves takes 16 rows of one matrix's output (the
+// matrix's row blocks on one XCD, so Phi comes from memory once per matrix); wave w owns
+// columns [16 w, 16 w + 16).  The A operand is the row block of S_c staged in LDS (rows padded
+// to DK + 8 floats, so each lane's 16-byte read is conflict-free), the B operand Phi's column
+// slab from memory.  The contraction index is visited in the order that lets each lane read
+// its A values as one 16-byte load: at step 4 kk + i, lane group gq = lane / 16 takes
+// k = 16 kk + 4 gq + i.
+template <int DK>
+__global__ void __launch_bounds__(DK * 4)
 state_compose_kernel(const float* __restrict__ S_c, const float* __restrict__ Phi,
-                     const float* __restrict__ log_scale, const float* S_hat, float* out, int dv, int dk)
+                     const float* __restrict__ log_scale, const float* S_hat, float* out, int N, int dv)
 {
-    __shared__ float sA[64][32 + 1];
-    __shared__ float sB[32][64 + 4];
-    const int tiles_c = dk / 64, tiles = (dv / 64) * tiles_c;
-    const int n = blockIdx.x / tiles;
-    const int t = blockIdx.x % tiles;
-    const int r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
-    const float* A = S_c + (size_t)n * dv * dk;
-    const float* P = Phi + (size_t)n * dk * dk;
-    const int tid = threadIdx.x;
-    const int tr = tid >> 4, tc = tid & 15;
-    const float scale = log_scale ? expf(log_scale[n]) : 1.f;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < dk; k0 += 32) {
-        for (int i = tid; i < 64 * 32; i += 256) {
-            sA[i >> 5][i & 31] = A[(size_t)(r0 + (i >> 5)) * dk + k0 + (i & 31)];
-            sB[i >> 6][i & 63] = P[(size_t)(k0 + (i >> 6)) * dk + c0 + (i & 63)];
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < 32; ++kk) {
-            float a[4], b[4];
+    constexpr int NW = DK / 16;                         // waves, one per 16 columns
+    constexpr int SR = DK + 8;
+    constexpr int KS = DK / 4;                          // MFMA steps
+    __shared__ __align__(16) float sA[16 * SR];
+    int n, rb;
+    xcd_item((int)blockIdx.x, dv / 16, n, rb);
+    if (n >= N) return;
+    const int tid = (int)threadIdx.x;
+    const int w = tid / 64, lane = tid % 64, m = lane % 16, gq = lane / 16;
+    const float* A = S_c + ((size_t)n * dv + (size_t)rb * 16) * DK;
+    const float* P = Phi + (size_t)n * DK * DK + 16 * w + m;
+    float bv[KS];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { a[i] = sA[4 * tr + i][kk]; b[i] = sB[kk][4 * tc + i]; }
+    for (int v = 0; v < KS; ++v) bv[v] = P[(size_t)(16 * (v / 4) + 4 * gq + v % 4) * DK];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
+    for (int i = 0; i < 16 * DK / 4 / (NW * 64); ++i) {
+        const int idx = (tid + NW * 64 * i) * 4;
+        *reinterpret_cast<f32x4*>(&sA[(idx / DK) * SR + idx % DK]) = *reinterpret_cast<const f32x4*>(A + idx);
     }
+    __syncthreads();
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < DK / 16; ++kk) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sA[m * SR + 16 * kk + 4 * gq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (kk % 2 == 0) a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bv[4 * kk + i], a0, 0, 0, 0);
+            else a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], bv[4 * kk + i], a1, 0, 0, 0);
+        }
+    }
+    const f32x4 acc = a0 + a1;
+    const float scale = log_scale ? expf(log_scale[n]) : 1.f;
+    // accumulator layout: lane (m, gq) holds rows 4 gq + i of column 16 w + m
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const size_t off = (size_t)n * dv * dk + (size_t)(r0 + 4 * tr + i) * dk + c0 + 4 * tc;
-        f32x4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = scale * acc[i][j];
-        if (S_hat) x += *reinterpret_cast<const f32x4*>(S_hat + off);
-        *reinterpret_cast<f32x4*>(out + off) = x;
+        const size_t off = ((size_t)n * dv + 16 * rb + 4 * gq + i) * DK + 16 * w + m;
+        float x = scale * acc[i];
+        if (S_hat) x += S_hat[off];
+        out[off] = x;
     }
 }
 
@@ -128,9 +135,16 @@ gdn_decode_kernel(const DecodeArgs a)
 
 hipError_t launch_state_compose(const float* S_c, const float* Phi, const float* log_scale, const float* S_hat,
                                 float* out, int N, int dv, int dk, hipStream_t stream) {
-    const unsigned blocks = (unsigned)N * (unsigned)((dv / 64) * (dk / 64));
-    hipLaunchKernelGGL(state_compose_kernel, dim3(blocks), dim3(256), 0, stream, S_c, Phi, log_scale, S_hat, out,
-                       dv, dk);
+    const long long blocks = xcd_grid(N, dv / 16);
+    if (blocks > 0x7fffffffLL || dv % 16 != 0) return hipErrorInvalidValue;
+    if (dk == 128)
+        hipLaunchKernelGGL((state_compose_kernel<128>), dim3((unsigned)blocks), dim3(512), 0, stream, S_c, Phi, log_scale,
+                           S_hat, out, N, dv);
+    else if (dk == 64)
+        hipLaunchKernelGGL((state_compose_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, stream, S_c, Phi, log_scale,
+                           S_hat, out, N, dv);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

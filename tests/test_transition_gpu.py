@@ -139,10 +139,15 @@ def test_compose_matches_definition():
     state_compose(S_c.cuda(), phi.cuda(), acc, out=acc)
     torch.cuda.synchronize()
     assert rel(np64(acc), ref + S_hat.double().numpy()) <= 1e-5
-    # dv != dk
-    A = torch.randn((3, 64, 128), generator=gen)
-    P = torch.randn((3, 128, 128), generator=gen) * 0.1
-    assert rel(np64(state_compose(A.cuda(), P.cuda())), A.double().numpy() @ P.double().numpy()) <= 1e-5
+    # dv != dk, both head sizes, and a log scale
+    for dv, dk, N in ((64, 128, 3), (128, 64, 5), (64, 64, 9)):
+        A = torch.randn((N, dv, dk), generator=gen)
+        P = torch.randn((N, dk, dk), generator=gen) * 0.1
+        ref = A.double().numpy() @ P.double().numpy()
+        assert rel(np64(state_compose(A.cuda(), P.cuda())), ref) <= 1e-5
+        ls = -torch.rand((N,), generator=gen) * 3
+        got = state_compose(A.cuda(), P.cuda(), log_scale=ls.cuda())
+        assert rel(np64(got), np.exp(ls.double().numpy())[:, None, None] * ref) <= 1e-5
 
 
 def test_checkpoint_composition_on_gpu():
