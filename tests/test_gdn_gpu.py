@@ -285,6 +285,41 @@ def test_split_schedule_empty_sequences_and_workspace_reuse():
         set_gdn_schedule(prev)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_random_configurations(case):
+    # Seeded draws over the supported set: 1-9 sequences of 0-700 tokens, Hqk in {1, 2, 4} with
+    # 1, 2 or 4 value heads per query/key head, dk and dv in {64, 128}, a given state or zero,
+    # with or without outputs.  Both schedules must give the same bits and meet the bounds.
+    rng = np.random.default_rng(1000 + case)
+    lens = [int(x) for x in rng.integers(0, 701, size=int(rng.integers(1, 10)))]
+    Hqk = int(rng.choice([1, 2, 4]))
+    Hv = Hqk * int(rng.choice([1, 2, 4]))
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    with_state = bool(rng.integers(0, 2))
+    want_o = bool(rng.integers(0, 2))
+    q_scale = float(rng.uniform(0.3, 1.5))
+    inp = synthetic.gdn_inputs(lens, Hqk, Hv, dk, dv, seed=2000 + case)
+    s_in = (rng.standard_normal((len(lens), Hv, dv, dk)) * 0.3).astype(np.float32) if with_state else None
+    d = inp.to("cuda")
+    s_dev = None if s_in is None else torch.from_numpy(s_in).cuda()
+    run = lambda: gdn_replay(d.q, d.k, d.v, d.g, d.beta, inp.cu_seqlens, q_scale=q_scale,  # noqa: E731
+                             state_in=s_dev, want_o=want_o)
+    S_f, o_f = _with_schedule("fused", run)
+    S_s, o_s = _with_schedule("split", run)
+    torch.cuda.synchronize()
+    label = "lens %s Hqk %d Hv %d dk %d dv %d state %s o %s" % (lens, Hqk, Hv, dk, dv, with_state, want_o)
+    assert torch.equal(S_f, S_s), label
+    if want_o:
+        assert torch.equal(o_f, o_s), label
+    S_ref, o_ref = oracle.gdn(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.g), np64(inp.beta),
+                              inp.cu_seqlens.numpy(), q_scale=q_scale,
+                              state_in=None if s_in is None else s_in.astype(np.float64))
+    es, eo = worst_errors(np64(S_f), np64(o_f) if want_o else None, S_ref, o_ref if want_o else None,
+                          inp.cu_seqlens.numpy())
+    print("%s: state %.2e output %.2e" % (label, es, eo), flush=True)
+    assert es <= STATE_TOL and eo <= OUT_TOL, label
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_orthonormal_keys_recall_exactly(d, schedule):
     # alpha = beta = 1 and the keys the standard basis, in a shuffled order: each token
