@@ -320,6 +320,20 @@ def test_random_configurations(case):
     assert es <= STATE_TOL and eo <= OUT_TOL, label
 
 
+@pytest.mark.parametrize("case", range(4))
+def test_fp32_random_configurations(case):
+    # the fp32-input path over seeded draws like test_random_configurations, at 1e-5
+    rng = np.random.default_rng(4000 + case)
+    lens = [int(x) for x in rng.integers(0, 401, size=int(rng.integers(1, 7)))]
+    Hqk = int(rng.choice([1, 2]))
+    Hv = Hqk * int(rng.choice([1, 2, 4]))
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    inp = synthetic.gdn_inputs(lens, Hqk, Hv, dk, dv, dtype=torch.float32, seed=4100 + case)
+    s_in = (rng.standard_normal((len(lens), Hv, dv, dk)) * 0.3).astype(np.float32) if rng.integers(0, 2) else None
+    run_and_compare(inp, state_in=s_in, q_scale=float(rng.uniform(0.3, 1.5)), stol=F32_TOL, otol=F32_TOL,
+                    label="fp32 lens %s Hqk %d Hv %d dk %d dv %d" % (lens, Hqk, Hv, dk, dv))
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_orthonormal_keys_recall_exactly(d, schedule):
     # alpha = beta = 1 and the keys the standard basis, in a shuffled order: each token

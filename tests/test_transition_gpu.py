@@ -99,6 +99,37 @@ def test_transition_in_segments(lens, Hv, min_segments):
         assert np.array_equal(np64(psi[lens.index(0), 0]), np.eye(d))
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_transition_random_configurations(case):
+    # Seeded draws: 1-6 spans of 0-2,500 tokens, Hqk in {1, 2} with 1, 2 or 4 value heads each,
+    # d in {64, 128}, bf16 or fp32 keys, the decay applied or kept apart.  Whether and how the
+    # spans are cut into segments follows from the draw.
+    rng = np.random.default_rng(3000 + case)
+    lens = [int(x) for x in rng.integers(0, 2501, size=int(rng.integers(1, 7)))]
+    Hqk = int(rng.choice([1, 2]))
+    Hv = Hqk * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.float32 if rng.integers(0, 2) else torch.bfloat16
+    separate = bool(rng.integers(0, 2))
+    inp = synthetic.gdn_inputs(lens, Hqk, Hv, d, d, dtype=dtype, seed=3100 + case)
+    dev = inp.to("cuda")
+    label = "lens %s Hqk %d Hv %d d %d %s separate %s" % (lens, Hqk, Hv, d, dtype, separate)
+    cu = inp.cu_seqlens.numpy()
+    if separate:
+        psi, ls = gdn_transition(dev.k, dev.g, dev.beta, inp.cu_seqlens, separate_decay=True)
+        torch.cuda.synchronize()
+        ref, ls_ref = oracle_phi_separated(np64(inp.k), np64(inp.g), np64(inp.beta), cu, d)
+        np.testing.assert_allclose(np64(ls), ls_ref, rtol=1e-5, atol=1e-5, err_msg=label)
+        got = psi
+    else:
+        got = gdn_transition(dev.k, dev.g, dev.beta, inp.cu_seqlens)
+        torch.cuda.synchronize()
+        ref = oracle_phi(np64(inp.k), np64(inp.g), np64(inp.beta), cu, d)
+    worst = max(rel(np64(got[b, h]), ref[b, h]) for b in range(len(lens)) for h in range(Hv))
+    print("%s: worst %.2e" % (label, worst), flush=True)
+    assert worst <= PHI_TOL, label
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_transition_of_reflectors(dtype):
     # alpha = 1 and beta = 2 make every factor I - 2 k k^T a Householder reflector (for unit
