@@ -243,6 +243,20 @@ def test_group_replay_small():
     assert torch.equal(S, S2)
 
 
+@pytest.mark.parametrize("case", range(4))
+def test_group_replay_random_configurations(case):
+    # Seeded draws: 1-5 groups of 1-3 layers, 1-400 tail tokens, d_model in {128, ..., 512},
+    # Hqk in {1, 2} with 1, 2 or 4 value heads each; every stage of every group checked
+    rng = np.random.default_rng(5000 + case)
+    G, L = int(rng.integers(1, 6)), int(rng.integers(1, 4))
+    n = int(rng.integers(1, 401))
+    d = 128 * int(rng.integers(1, 5))
+    Hqk = int(rng.choice([1, 2]))
+    Hv = Hqk * int(rng.choice([1, 2, 4]))
+    _group_case(G, L, n, d, Hqk, Hv, seed=5100 + case, e2e_groups=tuple(range(G)),
+                label="random G %d L %d n %d d %d Hqk %d Hv %d" % (G, L, n, d, Hqk, Hv), w_std=0.05)
+
+
 def test_group_replay_more_groups_than_one_launch_takes():
     # 18 groups: the per-group weight tables of one launch hold 16, so every stage runs as two
     # launches; groups on both sides of the split are checked at every stage
