@@ -28,7 +28,7 @@ import numpy as np
 
 from oracle.rounding import round_bf16, round_f32
 
-CH = 64          # tokens per chunk
+CH = 64          # tokens per chunk (the kernel's); chunk_replay takes others for the algebra pin
 BLK = 16         # diagonal block size of the inverse
 
 
@@ -43,6 +43,7 @@ def _split(x, b):
 
 
 def _inverse(L, f, b, mode):
+    CH = L.shape[0]
     """A = (I + L)^{-1} for a strictly lower triangular 64x64 L: the 16x16 diagonal blocks
     first, then block column j of A - I by merges A_ij = -A_ii sum_{k=j}^{i-1} L_ik A_kj.
     Returns N = A - I (fp32 values) as the kernel forms it."""
@@ -69,9 +70,10 @@ def _inverse(L, f, b, mode):
     return N
 
 
-def chunk_replay(q, k, v, g, beta, q_scale=1.0, mode="plan", state=None, drop=()):
+def chunk_replay(q, k, v, g, beta, q_scale=1.0, mode="plan", state=None, drop=(), ch=CH):
     """Replay one (sequence, head) in chunks.  q, k: [T, dk]; v: [T, dv]; g, beta: [T]
     (values exactly representable, e.g. bf16 inputs as float64).  Returns (S [dv, dk], O [T, dv]).
+    `ch` is the chunk length (a multiple of 16; the kernel's is 64).
     `drop` takes single choices out of the plan: "unit_diag" (fold A's unit diagonal into the
     bf16 operands), "split_pu" (P and U' single bf16 in P U'), "split_update" (U' diag(dec)
     single bf16 in the state update)."""
@@ -85,6 +87,7 @@ def chunk_replay(q, k, v, g, beta, q_scale=1.0, mode="plan", state=None, drop=()
     dv = v.shape[1]
     S = np.zeros((dv, dk)) if state is None else np.array(state, dtype=np.float64)
     O = np.zeros((T, dv))
+    CH = ch
     for c0 in range(0, T, CH):
         n = min(CH, T - c0)
         qc = np.zeros((CH, dk)); kc = np.zeros((CH, dk)); vc = np.zeros((CH, dv))

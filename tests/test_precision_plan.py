@@ -52,6 +52,17 @@ def test_chunked_algebra_is_the_token_recurrence(case):
     assert es < 1e-10 and eo < 1e-10
 
 
+@pytest.mark.parametrize("ch", [16, 32])
+def test_chunked_algebra_holds_at_other_chunk_lengths(case, ch):
+    # the WY form does not depend on the chunk length: without rounding, chunks of 16 and 32
+    # tokens (one diagonal block; two blocks and one merge) give the token recurrence too
+    arr, S_ref, O_ref = case
+    for h in range(HEADS):
+        S, O = chunk_replay(arr["q"][:, h], arr["k"][:, h], arr["v"][:, h], arr["g"][:, h], arr["beta"][:, h],
+                            mode="exact", ch=ch)
+        assert rel(S, S_ref[0, h]) < 1e-10 and rel(O, O_ref[:, h]) < 1e-10
+
+
 def test_plan_meets_the_bf16_tolerances(case):
     es, eo = errors(case, "plan")
     assert es <= 2e-3 and eo <= 3e-3
